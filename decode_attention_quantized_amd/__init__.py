@@ -1,0 +1,186 @@
+"""Python binding of libkvq: INT8 paged KV cache writes and split-KV decode attention on MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels of ``libkvq.so`` (built from
+``csrc/`` by ``build.py``).  PyTorch provides device memory and the current HIP stream; the
+library itself never allocates.  Importing this package fails if the library is missing.
+
+    cache = Cache("int8", num_blocks, num_kv_heads, head_dim)          # device planes
+    write(cache, k, v, slot_mapping)                                   # quantize-on-write
+    out, lse = decode(cache, q, block_tables, context_lens, max_context_len)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["Cache", "KvqError", "write", "decode", "workspace_bytes", "choose_num_splits", "page_offset",
+           "status_string", "lib", "LIB_PATH", "INT8", "BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+INT8, BF16 = 0, 1
+PAGE = 16
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_attention_quantized_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_P = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class _CacheDesc(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("num_blocks", _i32), ("block_size", _i32), ("num_kv_heads", _i32),
+                ("head_dim", _i32), ("k", _P), ("v", _P), ("k_scales", _P), ("v_scales", _P)]
+
+
+lib = ctypes.CDLL(LIB_PATH)
+_CP = ctypes.POINTER(_CacheDesc)
+lib.kvq_write.argtypes = [_CP, _P, _P, _P, _i32, _P]
+lib.kvq_write.restype = ctypes.c_int
+lib.kvq_check_write.argtypes = [_CP, _P, _P, _P, _i32, _P]
+lib.kvq_check_write.restype = ctypes.c_int
+lib.kvq_decode_workspace_bytes.argtypes = [_CP, _i32, _i32, _i32]
+lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.kvq_choose_num_splits.argtypes = [_CP, _i32, _i32, _i32]
+lib.kvq_choose_num_splits.restype = _i32
+_DEC = [_CP, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _P, _P, _P, ctypes.c_size_t, _P]
+lib.kvq_decode_attention.argtypes = _DEC
+lib.kvq_decode_attention.restype = ctypes.c_int
+lib.kvq_check_decode.argtypes = _DEC
+lib.kvq_check_decode.restype = ctypes.c_int
+lib.kvq_page_offset.argtypes = [_i32, _i32, _i32, _i32, _i32]
+lib.kvq_page_offset.restype = _i32
+lib.kvq_status_string.argtypes = [ctypes.c_int]
+lib.kvq_status_string.restype = ctypes.c_char_p
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+def status_string(status: int) -> str:
+    return lib.kvq_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise KvqError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Cache:
+    """One layer's paged KV cache pool in device memory (layout of include/kvq.h).
+
+    k, v: int8 [num_blocks][Hkv][16*D] (INT8) or bf16 bits as int16 [num_blocks][Hkv][16*D];
+    k_scales, v_scales: fp16 [num_blocks][Hkv][16][D/32] (INT8 only).
+    """
+
+    def __init__(self, dtype: str, num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda"):
+        if dtype not in ("int8", "bf16"):
+            raise ValueError(dtype)
+        self.dtype = dtype
+        self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
+        shape = (num_blocks, num_kv_heads, PAGE * head_dim)
+        if dtype == "int8":
+            self.k = torch.empty(shape, dtype=torch.int8, device=device)
+            self.v = torch.empty(shape, dtype=torch.int8, device=device)
+            sshape = (num_blocks, num_kv_heads, PAGE, head_dim // 32)
+            self.k_scales = torch.empty(sshape, dtype=torch.float16, device=device)
+            self.v_scales = torch.empty(sshape, dtype=torch.float16, device=device)
+        else:
+            self.k = torch.empty(shape, dtype=torch.int16, device=device)
+            self.v = torch.empty(shape, dtype=torch.int16, device=device)
+            self.k_scales = self.v_scales = None
+        self.desc = _CacheDesc(INT8 if dtype == "int8" else BF16, num_blocks, PAGE, num_kv_heads, head_dim,
+                               _ptr(self.k), _ptr(self.v), _ptr(self.k_scales), _ptr(self.v_scales))
+
+    def fill(self, code: int = 0x7F, scale_bits: int = 0x7BFF, bf16_bits: int = 0x7FC0):
+        """Fill every byte of the pool with a poison pattern (codes, scale bits or bf16 bits)."""
+        def s16(x):
+            return x - 65536 if x >= 32768 else x
+        if self.dtype == "int8":
+            c = code - 256 if code >= 128 else code
+            self.k.fill_(c)
+            self.v.fill_(c)
+            self.k_scales.view(torch.int16).fill_(s16(scale_bits))
+            self.v_scales.view(torch.int16).fill_(s16(scale_bits))
+        else:
+            self.k.fill_(s16(bf16_bits))
+            self.v.fill_(s16(bf16_bits))
+        return self
+
+
+def _as_bits16(t):
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"expected bfloat16 (or raw 16-bit) tensor, got {t.dtype}")
+
+
+def write(cache: Cache, k, v, slot_mapping, *, checked: bool = False, stream=None) -> None:
+    """Quantize-on-write (INT8) or scatter copy (BF16) of k, v [T][Hkv][D] bf16 into their slots."""
+    k, v = _as_bits16(k), _as_bits16(v)
+    T = int(slot_mapping.shape[0])
+    if tuple(k.shape) != (T, cache.num_kv_heads, cache.head_dim) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"k/v must be [{T}][{cache.num_kv_heads}][{cache.head_dim}]")
+    if slot_mapping.dtype != torch.int32 or not (k.is_contiguous() and v.is_contiguous()
+                                                 and slot_mapping.is_contiguous()):
+        raise ValueError("contiguous bf16 k/v and int32 slot_mapping required")
+    fn = lib.kvq_check_write if checked else lib.kvq_write
+    _check(fn(ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _stream(stream)), "kvq_write")
+
+
+def workspace_bytes(cache: Cache, num_seqs: int, num_q_heads: int, num_splits: int) -> int:
+    return int(lib.kvq_decode_workspace_bytes(ctypes.byref(cache.desc), num_seqs, num_q_heads, num_splits))
+
+
+def choose_num_splits(cache: Cache, num_seqs: int, num_q_heads: int, max_context_len: int) -> int:
+    r = int(lib.kvq_choose_num_splits(ctypes.byref(cache.desc), num_seqs, num_q_heads, max_context_len))
+    if r < 0:
+        raise KvqError(r, "kvq_choose_num_splits")
+    return r
+
+
+def page_offset(dtype: int, head_dim: int, which: int, token: int, channel: int) -> int:
+    return int(lib.kvq_page_offset(dtype, head_dim, which, token, channel))
+
+
+def decode(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int = 0, *,
+           out=None, lse=None, workspace=None, want_lse: bool = True, checked: bool = False, stream=None):
+    """Split-KV decode attention; returns (out fp32 [S][Hq][D], lse fp32 [S][Hq] or None)."""
+    q = _as_bits16(q)
+    S, Hq, D = (int(x) for x in q.shape)
+    if D != cache.head_dim or not q.is_contiguous():
+        raise ValueError("q must be contiguous [S][Hq][D] bf16")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if not (block_tables.is_contiguous() and context_lens.is_contiguous()) or block_tables.dim() != 2 \
+            or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables [S][max_blocks] and context_lens [S] required")
+    ns = num_splits if num_splits else choose_num_splits(cache, S, Hq, max_context_len)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(cache, S, Hq, ns)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    fn = lib.kvq_check_decode if checked else lib.kvq_decode_attention
+    st = fn(ctypes.byref(cache.desc), _ptr(q), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+            int(max_context_len), S, Hq, int(ns), _ptr(out), _ptr(lse), _ptr(workspace),
+            int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(st, "kvq_decode_attention")
+    return out, lse

@@ -1,0 +1,300 @@
+// C ABI of libkvq (declared in include/kvq.h): host-side validation, workspace sizing, the
+// split-count heuristic, launches on the caller's stream, and the checked (syncing) mode.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+#include "kvq_layout.h"
+
+namespace {
+
+constexpr int kMaxSplits = 4096;
+constexpr int kMaxGqa = 16;
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_cache(const kvq_cache_t *c) {
+  if (!c) return KVQ_ERR_INVALID_ARG;
+  if (c->dtype != KVQ_INT8_Q8_0 && c->dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (c->block_size != kvq::kPage) return KVQ_ERR_UNSUPPORTED;
+  if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
+  if ((int64_t)c->num_blocks * kvq::kPage > INT32_MAX) return KVQ_ERR_INVALID_ARG;
+  if (!c->k || !c->v || !aligned(c->k, 256) || !aligned(c->v, 256)) return KVQ_ERR_INVALID_ARG;
+  if (c->dtype == KVQ_INT8_Q8_0) {
+    if (!c->k_scales || !c->v_scales || !aligned(c->k_scales, 256) || !aligned(c->v_scales, 256))
+      return KVQ_ERR_INVALID_ARG;
+  }
+  return KVQ_OK;
+}
+
+int check_heads(const kvq_cache_t *c, int32_t num_q_heads) {
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+  if (num_q_heads / c->num_kv_heads > kMaxGqa) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Split count: enough workgroups to give every compute unit a few of them, but no split
+// shorter than a minimum number of pages, so that the merge stays small next to the stream.
+int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus) {
+  (void)dtype;
+  (void)D;
+  const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
+  if (max_pages <= 0) return 1;
+  const int64_t base = (int64_t)S * Hkv;
+  const int64_t target_wg = 2LL * cus;
+  int64_t ns = (target_wg + base - 1) / base;
+  const int min_pages = 8;
+  const int64_t cap = (max_pages + min_pages - 1) / min_pages;
+  if (ns > cap) ns = cap;
+  if (ns < 1) ns = 1;
+  if (ns > kMaxSplits) ns = kMaxSplits;
+  return (int)ns;
+}
+
+size_t workspace_bytes(int S, int Hq, int NS, int D) {
+  const size_t rows = (size_t)S * Hq * NS;
+  size_t o = rows * D * sizeof(float);
+  o = (o + 255) & ~(size_t)255;
+  return o + rows * 2 * sizeof(float);
+}
+
+int waves_for(int dtype, int D) {
+  (void)dtype;
+  (void)D;
+  return 4;
+}
+
+bool is_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return false;
+  return cs != hipStreamCaptureStatusNone;
+}
+
+bool bf16_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
+
+int decode_impl(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                int32_t num_splits, float *out, float *lse, void *workspace, size_t workspace_bytes_given,
+                void *stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = check_heads(cache, num_q_heads);
+  if (st != KVQ_OK) return st;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0) return KVQ_ERR_INVALID_ARG;
+  if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage)
+    return KVQ_ERR_INVALID_ARG;
+  if (num_splits < 0 || num_splits > kMaxSplits) return KVQ_ERR_INVALID_ARG;
+  if (!q || !block_tables || !context_lens || !out || !workspace) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(out, 16) ||
+      !aligned(workspace, 256) || (lse && !aligned(lse, 4)))
+    return KVQ_ERR_INVALID_ARG;
+  const int D = cache->head_dim, Hkv = cache->num_kv_heads;
+  const int NS = num_splits ? num_splits : choose_splits(cache->dtype, num_seqs, Hkv, D, max_context_len, device_cus());
+  if ((int64_t)num_seqs * Hkv * NS > INT32_MAX || (int64_t)num_seqs * num_q_heads * (D / 64) > INT32_MAX)
+    return KVQ_ERR_INVALID_ARG;
+  const size_t need = workspace_bytes(num_seqs, num_q_heads, NS, D);
+  if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
+  kvq::DecodeArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.kc = cache->k;
+  a.vc = cache->v;
+  a.ks = static_cast<const uint16_t *>(cache->k_scales);
+  a.vs = static_cast<const uint16_t *>(cache->v_scales);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  const size_t rows = (size_t)num_seqs * num_q_heads * NS;
+  const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
+  a.o_part = static_cast<float *>(workspace);
+  a.ml = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + o_bytes);
+  a.out = out;
+  a.lse = lse;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.S = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = Hkv;
+  a.G = num_q_heads / Hkv;
+  a.NB = cache->num_blocks;
+  a.NS = NS;
+  a.cpp = (max_pages + NS - 1) / NS;
+  a.D = D;
+  a.waves = waves_for(cache->dtype, D);
+  hipError_t e = kvq::launch_decode(cache->dtype, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH_FAILED;
+}
+
+int write_impl(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+               void *stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (num_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping || !aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 4))
+    return KVQ_ERR_INVALID_ARG;
+  const int per = cache->dtype == KVQ_INT8_Q8_0 ? 2 * (cache->head_dim / kvq::kGroup) : 2 * (cache->head_dim / 8);
+  if ((int64_t)num_tokens * cache->num_kv_heads * per > (int64_t)INT32_MAX * 256) return KVQ_ERR_INVALID_ARG;
+  kvq::WriteArgs a;
+  a.k = static_cast<const uint16_t *>(k);
+  a.v = static_cast<const uint16_t *>(v);
+  a.slot_mapping = slot_mapping;
+  a.kc = cache->k;
+  a.vc = cache->v;
+  a.ks = static_cast<uint16_t *>(cache->k_scales);
+  a.vs = static_cast<uint16_t *>(cache->v_scales);
+  a.T = num_tokens;
+  a.Hkv = cache->num_kv_heads;
+  a.D = cache->head_dim;
+  a.NB = cache->num_blocks;
+  hipError_t e = kvq::launch_kv_write(cache->dtype, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH_FAILED;
+}
+
+template <typename T>
+bool to_host(std::vector<T> &dst, const void *src, size_t n, hipStream_t st) {
+  dst.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st) != hipSuccess) return false;
+  return hipStreamSynchronize(st) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_write(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+              void *stream) {
+  return write_impl(cache, k, v, slot_mapping, num_tokens, stream);
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_splits) {
+  if (check_cache(cache) != KVQ_OK || check_heads(cache, num_q_heads) != KVQ_OK) return 0;
+  if (num_seqs <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
+  return workspace_bytes(num_seqs, num_q_heads, num_splits, cache->head_dim);
+}
+
+int32_t kvq_choose_num_splits(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_context_len) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = check_heads(cache, num_q_heads);
+  if (st != KVQ_OK) return st;
+  if (num_seqs <= 0 || max_context_len < 1) return KVQ_ERR_INVALID_ARG;
+  return choose_splits(cache->dtype, num_seqs, cache->num_kv_heads, cache->head_dim, max_context_len, device_cus());
+}
+
+int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
+                         void *workspace, size_t workspace_bytes_given, void *stream) {
+  return decode_impl(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                     num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+}
+
+int kvq_check_write(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping,
+                    int32_t num_tokens, void *stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (num_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  if (num_tokens == 0) return KVQ_OK;
+  if (!k || !v || !slot_mapping) return KVQ_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (is_capturing(s)) return KVQ_ERR_CAPTURING;
+  std::vector<int32_t> slots;
+  if (!to_host(slots, slot_mapping, (size_t)num_tokens, s)) return KVQ_ERR_LAUNCH_FAILED;
+  std::unordered_set<int32_t> seen;
+  const int64_t nslots = (int64_t)cache->num_blocks * kvq::kPage;
+  for (int32_t x : slots) {
+    if (x < 0) continue;
+    if (x >= nslots) return KVQ_ERR_VALIDATION_FAILED;
+    if (!seen.insert(x).second) return KVQ_ERR_VALIDATION_FAILED;
+  }
+  const size_t n = (size_t)num_tokens * cache->num_kv_heads * cache->head_dim;
+  std::vector<uint16_t> hk, hv;
+  if (!to_host(hk, k, n, s) || !to_host(hv, v, n, s)) return KVQ_ERR_LAUNCH_FAILED;
+  for (size_t i = 0; i < n; ++i)
+    if (!bf16_finite(hk[i]) || !bf16_finite(hv[i])) return KVQ_ERR_VALIDATION_FAILED;
+  st = write_impl(cache, k, v, slot_mapping, num_tokens, stream);
+  if (st != KVQ_OK) return st;
+  return hipStreamSynchronize(s) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH_FAILED;
+}
+
+int kvq_check_decode(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                     int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
+                     void *workspace, size_t workspace_bytes_given, void *stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = check_heads(cache, num_q_heads);
+  if (st != KVQ_OK) return st;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || !q || !block_tables || !context_lens) return KVQ_ERR_INVALID_ARG;
+  if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage)
+    return KVQ_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (is_capturing(s)) return KVQ_ERR_CAPTURING;
+  std::vector<int32_t> lens, tables;
+  if (!to_host(lens, context_lens, (size_t)num_seqs, s)) return KVQ_ERR_LAUNCH_FAILED;
+  if (!to_host(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq, s)) return KVQ_ERR_LAUNCH_FAILED;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int32_t L = lens[i];
+    if (L < 0 || L > max_context_len) return KVQ_ERR_VALIDATION_FAILED;
+    const int pages = (L + kvq::kPage - 1) / kvq::kPage;
+    for (int p = 0; p < pages; ++p) {
+      const int32_t b = tables[(size_t)i * max_blocks_per_seq + p];
+      if (b < 0 || b >= cache->num_blocks) return KVQ_ERR_VALIDATION_FAILED;
+    }
+  }
+  std::vector<uint16_t> hq;
+  if (!to_host(hq, q, (size_t)num_seqs * num_q_heads * cache->head_dim, s)) return KVQ_ERR_LAUNCH_FAILED;
+  for (uint16_t b : hq)
+    if (!bf16_finite(b)) return KVQ_ERR_VALIDATION_FAILED;
+  st = decode_impl(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
+                   num_splits, out, lse, workspace, workspace_bytes_given, stream);
+  if (st != KVQ_OK) return st;
+  return hipStreamSynchronize(s) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH_FAILED;
+}
+
+int32_t kvq_page_offset(int32_t dtype, int32_t head_dim, int32_t which, int32_t token, int32_t channel) {
+  if ((head_dim != 128 && head_dim != 256) || token < 0 || token >= kvq::kPage || channel < 0 ||
+      channel >= head_dim || (which != 0 && which != 1))
+    return -1;
+  if (dtype == KVQ_INT8_Q8_0) return (int32_t)(which ? kvq::i8_v_offset(token, channel) : kvq::i8_k_offset(token, channel));
+  if (dtype == KVQ_BF16)
+    return (int32_t)(which ? kvq::bf16_v_offset(token, channel) : kvq::bf16_k_offset(token, channel));
+  return -1;
+}
+
+const char *kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG";
+    case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_WORKSPACE_TOO_SMALL: return "KVQ_ERR_WORKSPACE_TOO_SMALL";
+    case KVQ_ERR_LAUNCH_FAILED: return "KVQ_ERR_LAUNCH_FAILED";
+    case KVQ_ERR_VALIDATION_FAILED: return "KVQ_ERR_VALIDATION_FAILED";
+    case KVQ_ERR_CAPTURING: return "KVQ_ERR_CAPTURING";
+    default: return "KVQ_ERR_UNKNOWN";
+  }
+}
+
+}  // extern "C"

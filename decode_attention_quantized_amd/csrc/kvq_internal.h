@@ -1,0 +1,35 @@
+// Internal interface between the C ABI (kvq_api.cpp) and the kernels (kvq_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+struct WriteArgs {
+  const uint16_t *k, *v;          // bf16 [T][Hkv][D]
+  const int32_t *slot_mapping;    // [T]
+  void *kc, *vc;                  // code / value planes
+  uint16_t *ks, *vs;              // fp16 scale planes (INT8 only)
+  int T, Hkv, D, NB;
+};
+
+struct DecodeArgs {
+  const uint16_t *q;              // bf16 [S][Hq][D]
+  const void *kc, *vc;            // code / value planes
+  const uint16_t *ks, *vs;        // fp16 scale planes (INT8 only)
+  const int32_t *block_tables;    // [S][max_blocks]
+  const int32_t *context_lens;    // [S]
+  float *o_part;                  // workspace: fp32 [S][Hq][NS][D]
+  float2 *ml;                     // workspace: (max in log2 units, sum) [S][Hq][NS]
+  float *out;                     // fp32 [S][Hq][D]
+  float *lse;                     // fp32 [S][Hq] or null
+  int max_blocks, max_context_len, S, Hq, Hkv, G, NB, NS, cpp, D;
+  int waves;                      // wavefronts per split workgroup (1, 2, 4 or 8)
+};
+
+// Each returns hipSuccess or the launch error.  dtype: 0 INT8, 1 BF16.
+hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream);
+hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kvq

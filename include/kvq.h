@@ -1,0 +1,177 @@
+/*
+ * kvq.h -- C ABI of libkvq: quantize-on-write into a paged INT8 KV cache, split-KV
+ * grouped-query decode attention over that cache, and the log-sum-exp merge, for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations and where they are defined:
+ *   kvq_write            quantize-on-write.  Half-the-memory page ("Making a ternary
+ *                        reasoning model fast in vLLM", anthonymorley.com), section "Is 8 bits
+ *                        enough?": llama.cpp's Q8_0 cache format, one scale per 32 values;
+ *                        gllm page (git.kenbook.uk/GlowLED/gllm), section "Quantization
+ *                        Design": symmetric int8, scale amax/127, round to nearest, clamp to
+ *                        +-127, dynamic per token; NVFP4 page (dev.to, "Building an NVFP4 KV
+ *                        cache ..."), section "Writing and reading the packed cache": BF16
+ *                        values plus a token-to-slot map, invalid slots do not write, valid
+ *                        slots unique within a call.
+ *   kvq_decode_attention split-KV decode attention and merge.  Long-context page ("long
+ *                        context attention and lessons", anthonymorley.com), section "Give more
+ *                        GPU workers a piece of the attention calculation": segments of the
+ *                        context computed in parallel, each giving a weighted value sum and its
+ *                        normalisation terms, combined with those terms; half-the-memory page,
+ *                        section "Read the compressed cache without copying it first": one
+ *                        query token reads the int8 cache directly, V dequantized in registers,
+ *                        no converted copy of the cache.
+ *   kvq_check_write,     checked wrappers.  NVFP4 page, section "Testing the cache without
+ *   kvq_check_decode     loading the model": a checked API that validates on the host,
+ *                        synchronises, and refuses graph capture; raw callers own stream
+ *                        ordering and cache lifetime.
+ *
+ * Arithmetic.  kvq_write: x = float(bf16); amax = max |x| over 32 consecutive channels of one
+ * (token, KV head); d = amax / 127 (IEEE fp32 division); s = fp16(min(d, 65504)), round to
+ * nearest even, stored; code = clamp(rint(x / s), -127, 127) in fp32 with ties to even,
+ * 0 when s == 0.  The decoded value is code * s.  kvq_decode_attention returns, per sequence s
+ * and query head hq (KV head h = hq / (Hq / Hkv)):
+ *   out[s][hq][:] = sum_t softmax_t(q . k_t / sqrt(D)) v_t   over t < context_lens[s]
+ *   lse[s][hq]    = ln sum_t exp(q . k_t / sqrt(D))            (natural log)
+ * computed with fp32 accumulation; an empty context gives out = 0 and lse = -inf.
+ *
+ * Cache layout (one kvq_cache_t per layer, all buffers owned by the caller, device memory):
+ *   INT8 (KVQ_INT8_Q8_0):
+ *     k, v           int8, num_blocks * Hkv pages of 16*D bytes, page (block b, KV head h)
+ *                    at byte offset (b*Hkv + h) * 16*D.  Inside a page the byte of token t
+ *                    (0..15) and channel c (0..D-1) is at
+ *                      K:  ((((c>>6)<<6) | (((c>>3)&3)<<4) | t) << 4) | (((c>>5)&1)<<3) | (c&7)
+ *                      V:  ((((c>>6)<<6) | ((t>>2)<<4) | (c&15)) << 4) | (((c>>4)&3)<<2) | (t&3)
+ *                    (kvq_page_offset() returns the same values).
+ *     k_scales,      binary16, [num_blocks][Hkv][16][D/32]: scale of (token t, group c/32).
+ *     v_scales
+ *   BF16 (KVQ_BF16):  k, v bfloat16, pages of 16*D values (2*16*D bytes); element of (t, c):
+ *                      K:  (((c>>5)<<6) | (((c>>3)&3)<<4) | t) << 3 | (c&7)
+ *                      V:  (((c>>5)<<6) | ((t>>2)<<4) | (c&15)) << 3 | (((c>>4)&1)<<2) | (t&3)
+ *                    k_scales = v_scales = NULL.
+ *   A slot is block*16 + offset; token t of sequence s is in slot
+ *   block_tables[s][t/16]*16 + t%16.  Every plane base must be 256-byte aligned.
+ *   Supported: block_size 16, head_dim 128 or 256, Hq % Hkv == 0, 1 <= Hq/Hkv <= 16.
+ *
+ * Errors.  Every entry point returns kvq_status_t (0 = KVQ_OK).  Host-side checks of
+ * scalars and pointers run before anything is enqueued; on error nothing is launched.
+ * No C++ exception crosses this interface.  The fast paths never allocate, free or
+ * synchronise and are safe to capture into a HIP graph.  The library writes only: the
+ * (slot, head) rows of valid slots in the cache, out, lse and the workspace.
+ *
+ * Streams are hipStream_t passed as void* (NULL = the default stream).  Device pointers
+ * are plain device addresses on the current HIP device.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_INT8_Q8_0 = 0, /* int8 codes + one binary16 scale per 32 values */
+  KVQ_BF16 = 1       /* bfloat16 values, no scales (comparison variant) */
+} kvq_dtype_t;
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1,         /* null/misaligned pointer, bad count or dimension */
+  KVQ_ERR_UNSUPPORTED = -2,         /* head_dim, block_size, dtype or GQA ratio not supported */
+  KVQ_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes below kvq_decode_workspace_bytes() */
+  KVQ_ERR_LAUNCH_FAILED = -4,       /* the HIP runtime reported an error */
+  KVQ_ERR_VALIDATION_FAILED = -5,   /* checked mode: device data broke the contract */
+  KVQ_ERR_CAPTURING = -6            /* checked mode called during stream capture */
+} kvq_status_t;
+
+typedef struct {
+  int32_t dtype;        /* kvq_dtype_t */
+  int32_t num_blocks;   /* pages per KV head in the pool */
+  int32_t block_size;   /* tokens per page; must be 16 */
+  int32_t num_kv_heads; /* Hkv */
+  int32_t head_dim;     /* D: 128 or 256 */
+  void *k, *v;          /* code / value planes (layout above) */
+  void *k_scales, *v_scales; /* binary16 scale planes (INT8), NULL for BF16 */
+} kvq_cache_t;
+
+/*
+ * Quantize-on-write (INT8) or scatter copy (BF16) of num_tokens new tokens.
+ *   k, v          device, bfloat16 [num_tokens][Hkv][D], contiguous, 16-byte aligned.
+ *   slot_mapping  device, int32 [num_tokens]; slot < 0 (or >= num_blocks*16): not written.
+ * Valid slots must be unique within one call (caller's contract; the fast path does not
+ * check it).  Writing a slot replaces every code and scale of that (slot, head) row.
+ * num_tokens == 0 is a no-op.  Asynchronous on `stream`.
+ */
+int kvq_write(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping,
+              int32_t num_tokens, void *stream);
+
+/*
+ * Bytes of workspace kvq_decode_attention needs for these sizes (num_splits 0 = the
+ * automatic choice for max_context_len given to kvq_choose_num_splits).  The workspace holds
+ * the split partials: fp32 weighted sums [S][Hq][splits][D] and (max, sum) pairs
+ * [S][Hq][splits][2].  Returns 0 on invalid arguments.
+ */
+size_t kvq_decode_workspace_bytes(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_splits);
+
+/*
+ * Split count the library uses when kvq_decode_attention gets num_splits == 0.  Depends only
+ * on the host-side sizes and the device's compute-unit count (no device synchronisation).
+ * Returns a negative kvq_status_t on invalid arguments.
+ */
+int32_t kvq_choose_num_splits(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t max_context_len);
+
+/*
+ * Split-KV decode attention for one query token per sequence, then the merge.
+ *   q                  device, bfloat16 [num_seqs][num_q_heads][D], 16-byte aligned.
+ *   block_tables       device, int32 [num_seqs][max_blocks_per_seq].
+ *   context_lens       device, int32 [num_seqs]; tokens 0..context_lens[s]-1 are attended
+ *                      (the token written by this step's kvq_write included); must satisfy
+ *                      0 <= context_lens[s] <= max_context_len.
+ *   max_context_len    host: upper bound of context_lens, sizes the grid without a sync;
+ *                      1 <= max_context_len <= max_blocks_per_seq*16.
+ *   num_splits         0 = automatic (kvq_choose_num_splits), else 1..4096.
+ *   out                device, fp32 [num_seqs][num_q_heads][D].
+ *   lse                device, fp32 [num_seqs][num_q_heads], or NULL.
+ *   workspace          device, at least kvq_decode_workspace_bytes(...) bytes, 256-byte
+ *                      aligned; its contents on entry do not matter.
+ * Context lengths and block ids outside the contract are clamped for memory safety (the
+ * result is then unspecified, no fault).  Asynchronous on `stream`.
+ */
+int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Checked mode (tests and debugging; not for hot loops).  Copies the metadata (and the bf16
+ * inputs) to the host, synchronises `stream`, rejects contract violations with
+ * KVQ_ERR_VALIDATION_FAILED before launching, then runs the fast path and synchronises
+ * again.  kvq_check_write rejects duplicate valid slots, slots >= num_blocks*16 and
+ * non-finite K/V.  kvq_check_decode rejects context_lens outside [0, max_context_len],
+ * block ids outside [0, num_blocks) in the pages a sequence uses, and non-finite Q.  Both
+ * refuse to run while `stream` is being captured (KVQ_ERR_CAPTURING).
+ */
+int kvq_check_write(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping,
+                    int32_t num_tokens, void *stream);
+int kvq_check_decode(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                     int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* In-page offset (bytes for INT8, elements for BF16) of (token 0..15, channel c) in a K
+ * (which = 0) or V (which = 1) page, per the layout above; -1 on invalid arguments. */
+int32_t kvq_page_offset(int32_t dtype, int32_t head_dim, int32_t which, int32_t token, int32_t channel);
+
+/* Human-readable name of a kvq_status_t. */
+const char *kvq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

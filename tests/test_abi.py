@@ -1,0 +1,139 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every declared symbol,
+rejects invalid arguments before launching anything, and its layout / sizing helpers agree
+with the documented formulas."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import decode_attention_quantized_amd as K
+from tests.layout import page_index
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+# Fake, 256-aligned, never dereferenced addresses: every call below fails host validation first.
+FAKE = 0x10000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported():
+    names = _declared()
+    assert "kvq_write" in names and "kvq_decode_attention" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert getattr(K.lib, n) is not None
+
+
+def test_status_strings():
+    for code, name in [(0, "KVQ_OK"), (-1, "KVQ_ERR_INVALID_ARG"), (-2, "KVQ_ERR_UNSUPPORTED"),
+                       (-3, "KVQ_ERR_WORKSPACE_TOO_SMALL"), (-4, "KVQ_ERR_LAUNCH_FAILED"),
+                       (-5, "KVQ_ERR_VALIDATION_FAILED"), (-6, "KVQ_ERR_CAPTURING")]:
+        assert K.status_string(code) == name
+    assert K.status_string(7) == "KVQ_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("dtype,dt", [("int8", K.INT8), ("bf16", K.BF16)])
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_page_offset_matches_documented_layout(dtype, dt, D, which):
+    idx = page_index(dtype, D, which)
+    got = np.array([[K.page_offset(dt, D, 0 if which == "k" else 1, t, c) for c in range(D)] for t in range(16)])
+    assert np.array_equal(got, idx)
+    # a bijection onto the page
+    assert np.array_equal(np.sort(idx.ravel()), np.arange(16 * D))
+
+
+def test_page_offset_rejects_bad_arguments():
+    assert K.page_offset(K.INT8, 64, 0, 0, 0) == -1
+    assert K.page_offset(K.INT8, 128, 2, 0, 0) == -1
+    assert K.page_offset(K.INT8, 128, 0, 16, 0) == -1
+    assert K.page_offset(K.INT8, 128, 0, 0, 128) == -1
+    assert K.page_offset(5, 128, 0, 0, 0) == -1
+
+
+def _desc(dtype=K.INT8, nb=64, bs=16, hkv=4, d=256, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE):
+    return K._CacheDesc(dtype, nb, bs, hkv, d, k, v, ks, vs)
+
+
+def _write(desc, k=FAKE, v=FAKE, sm=FAKE, T=1):
+    return K.lib.kvq_write(ctypes.byref(desc), k, v, sm, T, None)
+
+
+def _decode(desc, q=FAKE, bt=FAKE, mb=32, cl=FAKE, mcl=512, S=1, Hq=24, ns=4, out=FAKE, lse=None, ws=FAKE,
+            wsb=1 << 30):
+    return K.lib.kvq_decode_attention(ctypes.byref(desc), q, bt, mb, cl, mcl, S, Hq, ns, out, lse, ws, wsb, None)
+
+
+def test_write_rejects_invalid_arguments():
+    assert _write(_desc(d=64)) == -2
+    assert _write(_desc(bs=32)) == -2
+    assert _write(_desc(dtype=3)) == -2
+    assert _write(_desc(nb=0)) == -1
+    assert _write(_desc(hkv=0)) == -1
+    assert _write(_desc(k=None)) == -1
+    assert _write(_desc(k=FAKE + 16)) == -1            # plane base not 256-aligned
+    assert _write(_desc(ks=None)) == -1                # INT8 needs scale planes
+    assert _write(_desc(), k=None) == -1
+    assert _write(_desc(), v=FAKE + 2) == -1           # bf16 input not 16-aligned
+    assert _write(_desc(), sm=None) == -1
+    assert _write(_desc(), T=-1) == -1
+    assert _write(_desc(), T=0) == 0                   # no-op, nothing launched
+    assert K.lib.kvq_write(None, FAKE, FAKE, FAKE, 1, None) == -1
+
+
+def test_decode_rejects_invalid_arguments():
+    d = _desc()
+    assert _decode(d, Hq=25) == -1                     # Hq % Hkv != 0
+    assert _decode(_desc(hkv=1), Hq=17) == -2          # GQA ratio above 16
+    assert _decode(d, S=0) == -1
+    assert _decode(d, mb=0) == -1
+    assert _decode(d, mcl=0) == -1
+    assert _decode(d, mcl=32 * 16 + 1) == -1           # above max_blocks * 16
+    assert _decode(d, ns=-1) == -1
+    assert _decode(d, ns=4097) == -1
+    assert _decode(d, q=None) == -1
+    assert _decode(d, q=FAKE + 8) == -1
+    assert _decode(d, bt=None) == -1
+    assert _decode(d, cl=None) == -1
+    assert _decode(d, out=None) == -1
+    assert _decode(d, ws=None) == -1
+    assert _decode(d, ws=FAKE + 64) == -1              # workspace not 256-aligned
+    assert _decode(_desc(d=96)) == -2
+    need = K.lib.kvq_decode_workspace_bytes(ctypes.byref(d), 1, 24, 4)
+    assert need > 0
+    assert _decode(d, wsb=need - 1) == -3
+
+
+def test_workspace_bytes_formula():
+    d = _desc()
+    for S, Hq, ns, D in [(1, 24, 64, 256), (32, 32, 7, 128), (4, 24, 256, 256)]:
+        dd = _desc(d=D, hkv=8 if Hq == 32 else 4)
+        rows = S * Hq * ns
+        o = (rows * D * 4 + 255) // 256 * 256
+        assert K.lib.kvq_decode_workspace_bytes(ctypes.byref(dd), S, Hq, ns) == o + rows * 8
+    assert K.lib.kvq_decode_workspace_bytes(ctypes.byref(d), 1, 24, 0) == 0
+    assert K.lib.kvq_decode_workspace_bytes(ctypes.byref(d), 0, 24, 4) == 0
+    assert K.lib.kvq_decode_workspace_bytes(ctypes.byref(d), 1, 23, 4) == 0
+
+
+def test_split_heuristic_is_sane():
+    for S, Hkv, Hq, D, L in [(1, 4, 24, 256, 512), (1, 4, 24, 256, 4096), (1, 4, 24, 256, 32768),
+                             (4, 4, 24, 256, 32768), (32, 8, 32, 128, 8192), (1, 4, 24, 256, 1)]:
+        d = _desc(hkv=Hkv, d=D)
+        ns = K.lib.kvq_choose_num_splits(ctypes.byref(d), S, Hq, L)
+        pages = (L + 15) // 16
+        assert 1 <= ns <= 4096
+        assert ns <= max(1, pages)
+    assert K.lib.kvq_choose_num_splits(ctypes.byref(_desc()), 1, 24, 0) == -1
+    assert K.lib.kvq_choose_num_splits(ctypes.byref(_desc()), 1, 23, 64) == -1

@@ -1,0 +1,49 @@
+"""GPU parity at the full sizes of the long-context, mixed-batch and dense-8B workloads (one
+layer each), in the launch configuration the benchmark times: whole-cache byte comparison,
+and every output row against the oracle for each swept split count and the automatic one."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_quantized_amd as K
+import oracle as O
+import workloads as W
+from tests.gpu_util import Pair, assert_close, bf16_dev, dev, fill_from_layer, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cid", [3, 4, 5])
+def test_fullsize_int8(cid):
+    log(f"config {cid}: generating")
+    layer = W.make_layer(cid, 0)
+    cfg = layer.cfg
+    pair = Pair("int8", layer.num_blocks, cfg.num_kv_heads, cfg.head_dim)
+    log(f"config {cid}: writing {int(layer.context_lens.sum())} tokens")
+    fill_from_layer(pair, layer)
+    pair.assert_cache_equal()
+    mcl = int(layer.context_lens.max())
+    log(f"config {cid}: oracle decode")
+    ref = O.decode(pair.o, layer.q, layer.block_tables, layer.context_lens)
+    qd, btd, ld = bf16_dev(layer.q), dev(layer.block_tables), dev(layer.context_lens)
+    for ns in list(cfg.splits) + [0]:
+        log(f"config {cid}: decode splits={ns}")
+        out, lse = K.decode(pair.g, qd, btd, ld, mcl, ns)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref[0], ref[1], f"config {cid} ns={ns}")
+
+
+def test_fullsize_bf16_long_context():
+    layer = W.make_layer(3, 0)
+    cfg = layer.cfg
+    pair = Pair("bf16", layer.num_blocks, cfg.num_kv_heads, cfg.head_dim)
+    log("config 3 bf16: writing")
+    fill_from_layer(pair, layer)
+    pair.assert_cache_equal()
+    ref = O.decode(pair.o, layer.q, layer.block_tables, layer.context_lens)
+    for ns in (32, 0):
+        log(f"config 3 bf16: decode splits={ns}")
+        out, lse = K.decode(pair.g, bf16_dev(layer.q), dev(layer.block_tables), dev(layer.context_lens),
+                            int(layer.context_lens.max()), ns)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref[0], ref[1], f"config 3 bf16 ns={ns}")
