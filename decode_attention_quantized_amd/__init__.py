@@ -15,7 +15,7 @@ import os
 
 import torch
 
-__all__ = ["Cache", "KvqError", "write", "decode", "workspace_bytes", "choose_num_splits", "page_offset",
+__all__ = ["Cache", "KvqError", "write", "decode", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
            "status_string", "lib", "LIB_PATH", "INT8", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -50,6 +50,10 @@ lib.kvq_decode_attention.argtypes = _DEC
 lib.kvq_decode_attention.restype = ctypes.c_int
 lib.kvq_check_decode.argtypes = _DEC
 lib.kvq_check_decode.restype = ctypes.c_int
+lib.kvq_decode_partials.argtypes = [_CP, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _P, ctypes.c_size_t, _P]
+lib.kvq_decode_partials.restype = ctypes.c_int
+lib.kvq_decode_merge.argtypes = [_CP, _P, _i32, _i32, _i32, _i32, _P, ctypes.c_size_t, _P, _P, _P]
+lib.kvq_decode_merge.restype = ctypes.c_int
 lib.kvq_page_offset.argtypes = [_i32, _i32, _i32, _i32, _i32]
 lib.kvq_page_offset.restype = _i32
 lib.kvq_status_string.argtypes = [ctypes.c_int]
@@ -184,3 +188,23 @@ def decode(cache: Cache, q, block_tables, context_lens, max_context_len: int, nu
             int(workspace.numel() * workspace.element_size()), _stream(stream))
     _check(st, "kvq_decode_attention")
     return out, lse
+
+
+def decode_partials(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int, workspace,
+                    *, stream=None) -> None:
+    """First half of decode: split partials into ``workspace`` (num_splits must be explicit)."""
+    S, Hq, _ = (int(x) for x in q.shape)
+    st = lib.kvq_decode_partials(ctypes.byref(cache.desc), _ptr(q), _ptr(block_tables), int(block_tables.shape[1]),
+                                 _ptr(context_lens), int(max_context_len), S, Hq, int(num_splits), _ptr(workspace),
+                                 int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(st, "kvq_decode_partials")
+
+
+def decode_merge(cache: Cache, context_lens, max_context_len: int, num_seqs: int, num_q_heads: int, num_splits: int,
+                 workspace, out, lse=None, *, stream=None) -> None:
+    """Second half of decode: combine the partials in ``workspace`` into out (and lse)."""
+    st = lib.kvq_decode_merge(ctypes.byref(cache.desc), _ptr(context_lens), int(max_context_len), int(num_seqs),
+                              int(num_q_heads), int(num_splits), _ptr(workspace),
+                              int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
+                              _stream(stream))
+    _check(st, "kvq_decode_merge")

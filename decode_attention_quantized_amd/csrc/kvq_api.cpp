@@ -91,30 +91,29 @@ bool is_capturing(hipStream_t st) {
 
 bool bf16_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
 
-int decode_impl(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
-                const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
-                int32_t num_splits, float *out, float *lse, void *workspace, size_t workspace_bytes_given,
-                void *stream) {
+// Validates the decode arguments and fills the kernel argument block; no HIP call is made
+// unless num_splits == 0 (the heuristic reads the device's compute-unit count).
+int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                   const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_splits, float *out, float *lse, const void *workspace, size_t workspace_bytes_given,
+                   bool need_inputs, bool need_outputs, kvq::DecodeArgs &a) {
   int st = check_cache(cache);
   if (st != KVQ_OK) return st;
   st = check_heads(cache, num_q_heads);
   if (st != KVQ_OK) return st;
-  if (num_seqs <= 0 || max_blocks_per_seq <= 0) return KVQ_ERR_INVALID_ARG;
-  if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage)
+  if (num_seqs <= 0 || (need_inputs && max_blocks_per_seq <= 0)) return KVQ_ERR_INVALID_ARG;
+  if (max_context_len < 1 || (need_inputs && (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage))
     return KVQ_ERR_INVALID_ARG;
   if (num_splits < 0 || num_splits > kMaxSplits) return KVQ_ERR_INVALID_ARG;
-  if (!q || !block_tables || !context_lens || !out || !workspace) return KVQ_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(out, 16) ||
-      !aligned(workspace, 256) || (lse && !aligned(lse, 4)))
-    return KVQ_ERR_INVALID_ARG;
+  if (!context_lens || !workspace || !aligned(context_lens, 4) || !aligned(workspace, 256)) return KVQ_ERR_INVALID_ARG;
+  if (need_inputs && (!q || !block_tables || !aligned(q, 16) || !aligned(block_tables, 4))) return KVQ_ERR_INVALID_ARG;
+  if (need_outputs && (!out || !aligned(out, 16) || (lse && !aligned(lse, 4)))) return KVQ_ERR_INVALID_ARG;
   const int D = cache->head_dim, Hkv = cache->num_kv_heads;
   const int NS = num_splits ? num_splits : choose_splits(cache->dtype, num_seqs, Hkv, D, max_context_len, device_cus());
   if ((int64_t)num_seqs * Hkv * NS > INT32_MAX || (int64_t)num_seqs * num_q_heads * (D / 64) > INT32_MAX)
     return KVQ_ERR_INVALID_ARG;
-  const size_t need = workspace_bytes(num_seqs, num_q_heads, NS, D);
-  if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes_given < workspace_bytes(num_seqs, num_q_heads, NS, D)) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
-  kvq::DecodeArgs a;
   a.q = static_cast<const uint16_t *>(q);
   a.kc = cache->k;
   a.vc = cache->v;
@@ -124,8 +123,8 @@ int decode_impl(const kvq_cache_t *cache, const void *q, const int32_t *block_ta
   a.context_lens = context_lens;
   const size_t rows = (size_t)num_seqs * num_q_heads * NS;
   const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
-  a.o_part = static_cast<float *>(workspace);
-  a.ml = reinterpret_cast<float2 *>(static_cast<char *>(workspace) + o_bytes);
+  a.o_part = static_cast<float *>(const_cast<void *>(workspace));
+  a.ml = reinterpret_cast<float2 *>(static_cast<char *>(const_cast<void *>(workspace)) + o_bytes);
   a.out = out;
   a.lse = lse;
   a.max_blocks = max_blocks_per_seq;
@@ -139,8 +138,21 @@ int decode_impl(const kvq_cache_t *cache, const void *q, const int32_t *block_ta
   a.cpp = (max_pages + NS - 1) / NS;
   a.D = D;
   a.waves = waves_for(cache->dtype, D);
-  hipError_t e = kvq::launch_decode(cache->dtype, a, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH_FAILED;
+  return KVQ_OK;
+}
+
+int decode_impl(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                int32_t num_splits, float *out, float *lse, void *workspace, size_t workspace_bytes_given,
+                void *stream) {
+  kvq::DecodeArgs a;
+  int st = prepare_decode(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, true, true, a);
+  if (st != KVQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kvq::launch_decode_split(cache->dtype, a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
+  if (kvq::launch_decode_merge(a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
+  return KVQ_OK;
 }
 
 int write_impl(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
@@ -209,6 +221,30 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          void *workspace, size_t workspace_bytes_given, void *stream) {
   return decode_impl(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                      num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+}
+
+int kvq_decode_partials(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, void *workspace,
+                        size_t workspace_bytes_given, void *stream) {
+  kvq::DecodeArgs a;
+  int st = prepare_decode(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_splits, nullptr, nullptr, workspace, workspace_bytes_given, true, false, a);
+  if (st != KVQ_OK) return st;
+  return kvq::launch_decode_split(cache->dtype, a, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? KVQ_OK
+             : KVQ_ERR_LAUNCH_FAILED;
+}
+
+int kvq_decode_merge(const kvq_cache_t *cache, const int32_t *context_lens, int32_t max_context_len,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, const void *workspace,
+                     size_t workspace_bytes_given, float *out, float *lse, void *stream) {
+  kvq::DecodeArgs a;
+  int st = prepare_decode(cache, nullptr, nullptr, 0, context_lens, max_context_len, num_seqs, num_q_heads,
+                          num_splits, out, lse, workspace, workspace_bytes_given, false, true, a);
+  if (st != KVQ_OK) return st;
+  return kvq::launch_decode_merge(a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK
+                                                                                      : KVQ_ERR_LAUNCH_FAILED;
 }
 
 int kvq_check_write(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping,

@@ -30,6 +30,7 @@ struct DecodeArgs {
 
 // Each returns hipSuccess or the launch error.  dtype: 0 INT8, 1 BF16.
 hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream);
-hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace kvq

@@ -43,12 +43,12 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
 }
 
 // Four int8 codes (one dword) -> four exact f16 values, as two f16x2 words.
-// (x ^ 0x80) is x + 128 as an unsigned byte; 0x6400 | u is the f16 1024 + u; subtracting
-// 1152 gives x exactly.
+// (x ^ 0x80) is x + 128 as an unsigned byte u; v_perm places u under the exponent byte 0x64,
+// giving the f16 value 1024 + u; subtracting 1152 (one packed f16 add) gives x exactly.
 __device__ __forceinline__ void i8x4_to_f16(uint32_t w, uint32_t &lo, uint32_t &hi) {
   const uint32_t u = w ^ 0x80808080u;
-  const uint32_t a = (u & 0x000000FFu) | ((u & 0x0000FF00u) << 8) | 0x64006400u;
-  const uint32_t b = ((u & 0x00FF0000u) >> 16) | ((u & 0xFF000000u) >> 8) | 0x64006400u;
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // bytes 0, 1
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // bytes 2, 3
   const h2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) + bias);
   hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, b) + bias);
@@ -68,6 +68,20 @@ __device__ __forceinline__ f4_t mfma_f16(h8_t a, h8_t b, f4_t c) {
 
 __device__ __forceinline__ f4_t mfma_bf16(b8_t a, b8_t b, f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two P' values of one scale group, split for f16 MFMA operands: with s0, s1 the fp16 scales
+// in the low / high half of `s2`, hi = (f16(p0*s0), f16(p1*s1)) and lo = (f16(p0*s0 - hi0),
+// f16(p1*s1 - hi1)); each is one fused multiply-add rounded once to f16 (v_fma_mix{lo,hi}_f16).
+__device__ __forceinline__ void pprime2(float p0, float p1, uint32_t s2, uint32_t &hi, uint32_t &lo) {
+  uint32_t h, l;
+  // the first instruction of each pair defines the low half, the second the high half
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(h) : "v"(p0), "v"(s2));
+  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(s2));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,1,1]" : "=v"(l) : "v"(p0), "v"(s2), "v"(h));
+  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(s2), "v"(h));
+  hi = h;
+  lo = l;
 }
 
 // fp16 number e of a lane's scale block (packed in 16-byte words).
@@ -178,243 +192,66 @@ __global__ __launch_bounds__(256) void kv_write_bf16_kernel(WriteArgs a) {
 // ------------------------------------------------------------------ decode: split partials
 //
 // Workgroup (split j, KV head h, sequence s) of NW wavefronts.  The split owns pages
-// [j*cpp, min((j+1)*cpp, ceil(L/16))); the waves take 2-page units round-robin.  Within a
-// wavefront, lane l = 16*q4 + n16:
+// [j*cpp, min((j+1)*cpp, ceil(L/16))); the waves take units round-robin (INT8: 2 pages per
+// unit, BF16: 1 page).  Within a wavefront, lane l = 16*q4 + n16:
 //   Q.K   (A = K codes, B = Q):   lane holds scores of head n16, tokens 4*q4 .. 4*q4+3
 //   P.V   (A = P',      B = V):   A lane holds P' of head n16 for K-slots (page pg, token
 //                                 4*q4 + i) at element 4*pg + i -- the Q.K result layout
 //   acc   (P.V result):           lane holds heads 4*q4 .. 4*q4+3 of channel 16*jt + n16
+// Per unit: Q.K for the unit's pages, one softmax update (running max m, sum l, base 2), then
+// P.V; the accumulator is rescaled only when some head's maximum grew.  The next unit's
+// loads are issued as soon as the current unit's K (then V) registers are consumed.
 // Each split writes an unnormalised partial o = sum_t 2^(x_t - m) v_t with m = max_t x_t,
 // x_t = log2(e) * q.k_t / sqrt(D), and l = sum_t 2^(x_t - m).
-template <int D, int NW, bool I8>
-__global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a) {
-  constexpr int NG = D / kGroup;  // 32-channel groups / MFMA K-chunks
-  constexpr int NT = D / 16;      // 16-channel output tiles
-  constexpr int NL = I8 ? D / 64 : D / 32;  // 16-byte loads per lane per page
-  constexpr int NSW = NG / 2;     // 16-byte words of one lane's page scales (4 tokens x NG fp16)
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n16 = lane & 15, q4 = lane >> 4;
-  const int bid = blockIdx.x;
-  const int j = bid % a.NS;
-  const int h = (bid / a.NS) % a.Hkv;
-  const int s = bid / (a.NS * a.Hkv);
-  int L = a.context_lens[s];
-  L = max(0, min(L, a.max_context_len));
-  const int P = (L + kPage - 1) / kPage;
-  const int p0 = j * a.cpp;
-  const int p1 = min(p0 + a.cpp, P);
-  if (p0 >= p1) return;  // empty split: nothing written, the merge skips it
-  const int n_units = (p1 - p0 + 1) >> 1;
-  const int G = a.G;
-  const bool head_ok = n16 < G;
-  const int hq = h * G + (head_ok ? n16 : 0);
+typedef short s4_t __attribute__((ext_vector_type(4)));
 
-  // ---- Q operand (B of Q.K): lane holds head n16, channels 32g + 8*q4 + 0..7 of chunk g
-  const uint16_t *qrow = a.q + ((int64_t)s * a.Hq + hq) * D;
-  u4_t qraw[NG];
+// Max / sum over the four lane rows (lanes n, n+16, n+32, n+48) with the gfx950 row swaps.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x for x <= 0 (softmax weights); results below 2^-126 may flush to zero, which is far
+// below fp32 resolution next to the largest weight (1).
+__device__ __forceinline__ float exp2_w(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Buffer resource of one page or scale tile: loads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void *base, int64_t index, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(base)) + index * bytes, 0,
+                                           bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u4_t ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Q operand (B of Q.K): lane holds head n16 (zero when n16 >= G), channels 32g + 8*q4 + 0..7.
+template <int D>
+__device__ __forceinline__ void load_q(const DecodeArgs &a, int s, int h, int n16, int q4, bool head_ok,
+                                       u4_t (&qraw)[D / 32]) {
+  const uint16_t *qrow = a.q + ((int64_t)s * a.Hq + h * a.G + (head_ok ? n16 : 0)) * D;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
+  for (int g = 0; g < D / 32; ++g)
     qraw[g] = head_ok ? *reinterpret_cast<const u4_t *>(qrow + kGroup * g + 8 * q4) : u4_t{0u, 0u, 0u, 0u};
-  }
-  h8_t qop[I8 ? NG : 1];
-  b8_t qopb[I8 ? 1 : NG];
-  float cmul;
-  if constexpr (I8) {
-    float qmax = 0.0f;
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(qraw[g][e])), fabsf(bf16_hi(qraw[g][e]))));
-    qmax = fmaxf(qmax, __shfl_xor(qmax, 16));
-    qmax = fmaxf(qmax, __shfl_xor(qmax, 32));
-    int shift = 0;
-    if (qmax > 0.0f) {
-      int e2;
-      frexpf(qmax, &e2);
-      shift = 15 - e2;  // max |q| * 2^shift lies in [2^14, 2^15): exact in f16
-    }
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qop[g][2 * e] = (_Float16)ldexpf(bf16_lo(qraw[g][e]), shift);
-        qop[g][2 * e + 1] = (_Float16)ldexpf(bf16_hi(qraw[g][e]), shift);
-      }
-    cmul = head_ok ? ldexpf(kLog2e / sqrtf((float)D), -shift) : 0.0f;
-  } else {
-#pragma unroll
-    for (int g = 0; g < NG; ++g) qopb[g] = __builtin_bit_cast(b8_t, qraw[g]);
-    cmul = head_ok ? kLog2e / sqrtf((float)D) : 0.0f;
-  }
+}
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  f4_t acc[NT];
-#pragma unroll
-  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int32_t *btrow = a.block_tables + (int64_t)s * a.max_blocks;
-  constexpr int kPageBytes = kPage * D * (I8 ? 1 : 2);
-
-  for (int u = wave; u < n_units; u += NW) {
-    const int pa = p0 + 2 * u;
-    const bool b_ok = pa + 1 < p1;
-    int ba = btrow[pa];
-    int bb = b_ok ? btrow[pa + 1] : ba;
-    ba = min(max(ba, 0), a.NB - 1);
-    bb = min(max(bb, 0), a.NB - 1);
-    const int64_t pga = (int64_t)ba * a.Hkv + h, pgb = (int64_t)bb * a.Hkv + h;
-
-    // ---- loads: codes with one 16-byte load per lane per instruction (1 KiB per wave)
-    const u4_t *KA = reinterpret_cast<const u4_t *>(static_cast<const char *>(a.kc) + pga * kPageBytes) + lane;
-    const u4_t *KB = reinterpret_cast<const u4_t *>(static_cast<const char *>(a.kc) + pgb * kPageBytes) + lane;
-    const u4_t *VA = reinterpret_cast<const u4_t *>(static_cast<const char *>(a.vc) + pga * kPageBytes) + lane;
-    const u4_t *VB = reinterpret_cast<const u4_t *>(static_cast<const char *>(a.vc) + pgb * kPageBytes) + lane;
-    u4_t kA[NL], kB[NL], vA[NL], vB[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      kA[i] = KA[64 * i];
-      kB[i] = KB[64 * i];
-    }
-    u4_t ksA[I8 ? NSW : 1], ksB[I8 ? NSW : 1], vsA[I8 ? NSW : 1], vsB[I8 ? NSW : 1];
-    if constexpr (I8) {
-      const u4_t *SA = reinterpret_cast<const u4_t *>(a.ks + pga * (kPage * NG) + 4 * q4 * NG);
-      const u4_t *SB = reinterpret_cast<const u4_t *>(a.ks + pgb * (kPage * NG) + 4 * q4 * NG);
-#pragma unroll
-      for (int i = 0; i < NSW; ++i) {
-        ksA[i] = SA[i];
-        ksB[i] = SB[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      vA[i] = VA[64 * i];
-      vB[i] = VB[64 * i];
-    }
-    if constexpr (I8) {
-      const u4_t *SA = reinterpret_cast<const u4_t *>(a.vs + pga * (kPage * NG) + 4 * q4 * NG);
-      const u4_t *SB = reinterpret_cast<const u4_t *>(a.vs + pgb * (kPage * NG) + 4 * q4 * NG);
-#pragma unroll
-      for (int i = 0; i < NSW; ++i) {
-        vsA[i] = SA[i];
-        vsB[i] = SB[i];
-      }
-    }
-
-    // ---- Q.K^T: scores of head n16 for tokens 4*q4 + i of both pages
-    f4_t sc[2];
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      const u4_t(&kr)[NL] = pg ? kB : kA;
-      f4_t score = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (I8) {
-        const u4_t(&sr)[NSW] = pg ? ksB : ksA;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const h8_t av = i8x8_to_h8(kr[g >> 1][(g & 1) * 2], kr[g >> 1][(g & 1) * 2 + 1]);
-          const f4_t c = mfma_f16(av, qop[g], f4_t{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-          for (int i = 0; i < 4; ++i) score[i] = fmaf(scale_at(sr, i * NG + g), c[i], score[i]);
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) score = mfma_bf16(__builtin_bit_cast(b8_t, kr[g]), qopb[g], score);
-      }
-      sc[pg] = score;
-    }
-
-    // ---- masking and online softmax (base 2)
-    const bool unit_masked = !b_ok || (pa + 2) * kPage > L;
-    float x[8];
-    bool valid[8];
-#pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = (pa + pg) * kPage + 4 * q4 + i;
-        const bool ok = head_ok && (pg == 0 || b_ok) && tok < L;
-        valid[4 * pg + i] = (pg == 0 || b_ok) && tok < L;
-        x[4 * pg + i] = ok ? sc[pg][i] * cmul : -INFINITY;
-      }
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = (m_new == m_run) ? 1.0f : exp2f(m_run - m_use);
-    float p[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(x[e] - m_use);
-      psum += p[e];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.0f)) {
-      float ar[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * q4 + i);
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[jt][i] *= ar[i];
-    }
-
-    // ---- P.V
-    if constexpr (I8) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        h8_t phi, plo;
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * pg + i;
-            const float sv = valid[e] ? scale_at(pg ? vsB : vsA, i * NG + g) : 0.0f;
-            const float pp = p[e] * sv;
-            const _Float16 hi = (_Float16)pp;
-            phi[e] = hi;
-            plo[e] = (_Float16)fmaf(p[e], sv, -(float)hi);
-          }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int jt = 2 * g + jj;
-          const h8_t bv = i8x8_to_h8(vA[jt >> 2][jt & 3], vB[jt >> 2][jt & 3]);
-          acc[jt] = mfma_f16(phi, bv, acc[jt]);
-          acc[jt] = mfma_f16(plo, bv, acc[jt]);
-        }
-      }
-    } else {
-      b8_t phi, plo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 hi = (__bf16)p[e];
-        phi[e] = hi;
-        plo[e] = (__bf16)(p[e] - (float)hi);
-      }
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt) {
-        u4_t w = {vA[jt >> 1][(jt & 1) * 2], vA[jt >> 1][(jt & 1) * 2 + 1], vB[jt >> 1][(jt & 1) * 2],
-                  vB[jt >> 1][(jt & 1) * 2 + 1]};
-        if (unit_masked) {  // unwritten slots may hold any bits (NaN): zero them
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (!valid[e]) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        }
-        const b8_t bv = __builtin_bit_cast(b8_t, w);
-        acc[jt] = mfma_bf16(phi, bv, acc[jt]);
-        acc[jt] = mfma_bf16(plo, bv, acc[jt]);
-      }
-    }
-  }
-
-  // ---- per-head sum over the four lane rows
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-
+// Writes the partial of this wavefront (NW == 1) or of the whole workgroup (LDS merge).
+template <int D, int NW>
+__device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h, int j, int wave, int n16, int q4,
+                                              float m_run, float l_run, const f4_t (&acc)[D / 16]) {
+  constexpr int NT = D / 16;
+  const int G = a.G;
+  l_run = rows_sum(l_run);
   const int64_t row0 = ((int64_t)s * a.Hq + (int64_t)h * G) * a.NS + j;  // partial of head h*G + 0
   if constexpr (NW == 1) {
 #pragma unroll
@@ -424,23 +261,25 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a) {
         const int hh = 4 * q4 + i;
         if (hh < G) a.o_part[(row0 + (int64_t)hh * a.NS) * D + 16 * jt + n16] = acc[jt][i];
       }
-    if (q4 == 0 && head_ok) a.ml[row0 + (int64_t)n16 * a.NS] = make_float2(m_run, l_run);
+    if (q4 == 0 && n16 < G) a.ml[row0 + (int64_t)n16 * a.NS] = make_float2(m_run, l_run);
   } else {
     extern __shared__ float smem[];
-    float *s_acc = smem;                 // [NW][G][D]
-    float *s_m = smem + NW * G * D;      // [NW][16]
-    float *s_l = s_m + NW * 16;          // [NW][16]
+    float *s_acc = smem;             // [NW][G][D]
+    float *s_m = smem + NW * G * D;  // [NW][16]
+    float *s_l = s_m + NW * 16;      // [NW][16]
     if (q4 == 0) {
       s_m[wave * 16 + n16] = m_run;
       s_l[wave * 16 + n16] = l_run;
     }
+    if (4 * q4 < G) {
 #pragma unroll
-    for (int jt = 0; jt < NT; ++jt)
+      for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hh = 4 * q4 + i;
-        if (hh < G) s_acc[(wave * G + hh) * D + 16 * jt + n16] = acc[jt][i];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int hh = 4 * q4 + i;
+          if (hh < G) s_acc[(wave * G + hh) * D + 16 * jt + n16] = acc[jt][i];
+        }
+    }
     __syncthreads();
     for (int e = threadIdx.x; e < G * D; e += NW * 64) {
       const int hh = e / D, c = e - hh * D;
@@ -463,20 +302,350 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// ---- INT8 cache: 2-page units, f16 MFMA for both products
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_i8_kernel(DecodeArgs a) {
+  constexpr int NG = D / kGroup;      // scale groups
+  constexpr int NT = D / 16;          // output tiles
+  constexpr int NL = D / 64;          // 16-byte code loads per lane per page
+  constexpr int PAGE_B = kPage * D;   // bytes of one code page
+  constexpr int SCALE_B = kPage * NG * 2;  // bytes of one scale tile (= D)
+  __shared__ __attribute__((aligned(16))) h8_t s_q[NG][64];              // Q operand fragments
+  __shared__ __attribute__((aligned(16))) uint16_t s_sc[NW][4][NG][16];  // [wave][Ka,Kb,Va,Vb][group][token]
+  __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];
+
+  const int32_t *__restrict__ block_tables = a.block_tables;  // read-only: scalar loads
+  const int32_t *__restrict__ context_lens = a.context_lens;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int j = blockIdx.x % a.NS;
+  const int h = (blockIdx.x / a.NS) % a.Hkv;
+  const int s = blockIdx.x / (a.NS * a.Hkv);
+  const int L = max(0, min(context_lens[s], a.max_context_len));
+  const int P = (L + kPage - 1) / kPage;
+  const int p0 = j * a.cpp;
+  const int p1 = min(p0 + a.cpp, P);
+  if (p0 >= p1) return;  // empty split: nothing written, the merge skips it
+  const int n_units = (p1 - p0 + 1) >> 1;
+  const bool head_ok = n16 < a.G;
+
+  // Q: bf16 rescaled by 2^shift per head so that max |q| lies in [2^14, 2^15): exact in f16.
+  // Wave 0 converts the operand once into LDS ([group][lane] 16-byte fragments) for all waves.
+  int shift = 0;
+  {
+    u4_t qraw[NG];
+    load_q<D>(a, s, h, n16, q4, head_ok, qraw);
+    float qmax = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(qraw[g][e])), fabsf(bf16_hi(qraw[g][e]))));
+    qmax = rows_max(qmax);
+    if (qmax > 0.0f) {
+      int e2;
+      frexpf(qmax, &e2);
+      shift = 15 - e2;
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        h8_t qg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qg[2 * e] = (_Float16)ldexpf(bf16_lo(qraw[g][e]), shift);
+          qg[2 * e + 1] = (_Float16)ldexpf(bf16_hi(qraw[g][e]), shift);
+        }
+        s_q[g][lane] = qg;
+      }
+    }
+    __syncthreads();
+  }
+  const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f4_t acc[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
+  const int voff = lane * 16;  // byte offset of this lane's 16-byte fragment in each KiB of a page
+  auto page_index = [&](int p) -> int64_t {  // (block, head) page of logical page p, block id clamped
+    const int b = min(max(btrow[p], 0), a.NB - 1);
+    return (int64_t)b * a.Hkv + h;
+  };
+  u4_t kb[2][NL], vb[2][NL];
+  uint32_t ksb[2], vsb[2];
+  auto load_k = [&](int64_t pga, int64_t pgb) {
+    const auto ra = page_rsrc(a.kc, pga, PAGE_B), rb = page_rsrc(a.kc, pgb, PAGE_B);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      kb[0][i] = ld16(ra, voff, 1024 * i);
+      kb[1][i] = ld16(rb, voff, 1024 * i);
+    }
+    ksb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pga, SCALE_B), lane * 4, 0, 0);
+    ksb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pgb, SCALE_B), lane * 4, 0, 0);
+  };
+  auto load_v = [&](int64_t pga, int64_t pgb) {
+    const auto ra = page_rsrc(a.vc, pga, PAGE_B), rb = page_rsrc(a.vc, pgb, PAGE_B);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      vb[0][i] = ld16(ra, voff, 1024 * i);
+      vb[1][i] = ld16(rb, voff, 1024 * i);
+    }
+    vsb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pga, SCALE_B), lane * 4, 0, 0);
+    vsb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pgb, SCALE_B), lane * 4, 0, 0);
+  };
+  // Scale tile dword `lane` holds (token lane / (NG/2), groups 2*(lane % (NG/2)) and +1); it is
+  // stored transposed [group][token] so that a lane later reads its 4 tokens of a group with one
+  // 8-byte read.  Tokens at or past `lim` are stored as 0.
+  auto stage = [&](int slot, uint32_t w, int lim) {
+    if (lane < SCALE_B / 4) {
+      const int t = lane / (NG / 2), g = 2 * (lane % (NG / 2));
+      const bool ok = t < lim;
+      s_sc[wave][slot][g][t] = ok ? (uint16_t)(w & 0xFFFFu) : (uint16_t)0;
+      s_sc[wave][slot][g + 1][t] = ok ? (uint16_t)(w >> 16) : (uint16_t)0;
+    }
+  };
+  auto scales4 = [&](int slot, int g) -> u2_t {
+    return *reinterpret_cast<const u2_t *>(&s_sc[wave][slot][g][4 * q4]);
+  };
+
+  int u = wave;
+  if (u < n_units) {
+    const int pa = p0 + 2 * u;
+    const int64_t pga = page_index(pa), pgb = page_index(pa + 1 < p1 ? pa + 1 : pa);
+    load_k(pga, pgb);
+    load_v(pga, pgb);
+  }
+  for (; u < n_units; u += NW) {
+    const int pa = p0 + 2 * u;
+    const int lim_a = min(L - pa * kPage, kPage);                            // valid tokens of page a
+    const int lim_b = (pa + 1 < p1) ? min(L - (pa + 1) * kPage, kPage) : 0;  // of page b
+    const int un = u + NW;
+    const int pan = p0 + 2 * un;
+    int64_t pga_n = 0, pgb_n = 0;
+    if (un < n_units) {
+      pga_n = page_index(pan);
+      pgb_n = page_index(pan + 1 < p1 ? pan + 1 : pan);
+    }
+
+    // ---- Q.K^T for both pages: one MFMA per 32-channel group, then the group's fp16 scale
+    stage(0, ksb[0], kPage);
+    stage(1, ksb[1], kPage);
+    f4_t sc[2] = {f4_t{0.0f, 0.0f, 0.0f, 0.0f}, f4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    // Q fragments are re-read from LDS every unit rather than kept in 32 registers (a volatile
+    // LDS read, so that the compiler does not hoist these loop-invariant loads).
+    const volatile __attribute__((address_space(3))) h8_t *qlds =
+        (const volatile __attribute__((address_space(3))) h8_t *)(&s_q[0][0]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const h8_t qg = qlds[g * 64 + lane];
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        const h8_t av = i8x8_to_h8(kb[pg][g >> 1][(g & 1) * 2], kb[pg][g >> 1][(g & 1) * 2 + 1]);
+        const f4_t c = mfma_f16(av, qg, f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+        const u2_t sw = scales4(pg, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t hbits = (i & 1) ? (sw[i >> 1] >> 16) : (sw[i >> 1] & 0xFFFFu);
+          sc[pg][i] = fmaf(f16_bits_to_f32(hbits), c[i], sc[pg][i]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (un < n_units) load_k(pga_n, pgb_n);
+
+    // ---- online softmax over the unit's 32 tokens (base 2)
+    float x[8];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = head_ok && (4 * q4 + i) < (pg ? lim_b : lim_a);
+        x[4 * pg + i] = ok ? sc[pg][i] * cmul : -INFINITY;
+      }
+    float mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = rows_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = (m_new == m_run) ? 1.0f : exp2_w(m_run - m_use);
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = exp2_w(x[e] - m_use);
+      psum += p[e];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {  // some head's maximum grew: rescale its accumulator rows
+      if (q4 == 0) s_alpha[wave][n16] = alpha;
+      const f4_t ar = *reinterpret_cast<const f4_t *>(&s_alpha[wave][4 * q4]);
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) acc[jt] *= ar;
+    }
+
+    // ---- P.V: P' = p * s_v per (token, group) as f16 hi + lo, times exact f16 V codes
+    stage(2, vsb[0], lim_a);
+    stage(3, vsb[1], lim_b);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const u2_t sa = scales4(2, g), sb = scales4(3, g);
+      uint32_t hw[4], lw[4];
+      pprime2(p[0], p[1], sa[0], hw[0], lw[0]);
+      pprime2(p[2], p[3], sa[1], hw[1], lw[1]);
+      pprime2(p[4], p[5], sb[0], hw[2], lw[2]);
+      pprime2(p[6], p[7], sb[1], hw[3], lw[3]);
+      const h8_t phi = __builtin_bit_cast(h8_t, u4_t{hw[0], hw[1], hw[2], hw[3]});
+      const h8_t plo = __builtin_bit_cast(h8_t, u4_t{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jt = 2 * g + jj;
+        const h8_t bv = i8x8_to_h8(vb[0][jt >> 2][jt & 3], vb[1][jt >> 2][jt & 3]);
+        acc[jt] = mfma_f16(phi, bv, acc[jt]);
+        acc[jt] = mfma_f16(plo, bv, acc[jt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep each group's temporaries short-lived
+    }
+    if (un < n_units) load_v(pga_n, pgb_n);
+  }
+  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc);
+}
+
+// ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
+__device__ __forceinline__ f4_t mfma16_bf16(s4_t a, s4_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_split_bf16_kernel(DecodeArgs a) {
+  constexpr int NG = D / 32;  // 16-byte loads per lane per page (8 bf16 each)
+  constexpr int NT = D / 16;
+  constexpr int PAGE_B = kPage * D * 2;
+  __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];
+  const int32_t *__restrict__ block_tables = a.block_tables;
+  const int32_t *__restrict__ context_lens = a.context_lens;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int j = blockIdx.x % a.NS;
+  const int h = (blockIdx.x / a.NS) % a.Hkv;
+  const int s = blockIdx.x / (a.NS * a.Hkv);
+  const int L = max(0, min(context_lens[s], a.max_context_len));
+  const int P = (L + kPage - 1) / kPage;
+  const int p0 = j * a.cpp;
+  const int p1 = min(p0 + a.cpp, P);
+  if (p0 >= p1) return;
+  const int n_units = p1 - p0;
+  const bool head_ok = n16 < a.G;
+
+  u4_t qraw[NG];
+  load_q<D>(a, s, h, n16, q4, head_ok, qraw);
+  b8_t qop[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) qop[g] = __builtin_bit_cast(b8_t, qraw[g]);
+  const float cmul = kLog2e / sqrtf((float)D);
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f4_t acc[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
+  const int voff = lane * 16;
+  auto page_index = [&](int p) -> int64_t {
+    const int b = min(max(btrow[p], 0), a.NB - 1);
+    return (int64_t)b * a.Hkv + h;
+  };
+  u4_t kb[NG], vb[NG];
+  auto load = [&](u4_t(&dst)[NG], const void *base, int64_t pg) {
+    const auto r = page_rsrc(base, pg, PAGE_B);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) dst[i] = ld16(r, voff, 1024 * i);
+  };
+  int u = wave;
+  if (u < n_units) {
+    const int64_t pg = page_index(p0 + u);
+    load(kb, a.kc, pg);
+    load(vb, a.vc, pg);
+  }
+  for (; u < n_units; u += NW) {
+    const int lim = min(L - (p0 + u) * kPage, kPage);
+    const int un = u + NW;
+    const int64_t pgn = un < n_units ? page_index(p0 + un) : 0;
+
+    f4_t score = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) score = mfma_bf16(__builtin_bit_cast(b8_t, kb[g]), qop[g], score);
+    if (un < n_units) load(kb, a.kc, pgn);
+
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (head_ok && 4 * q4 + i < lim) ? score[i] * cmul : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = rows_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = (m_new == m_run) ? 1.0f : exp2_w(m_run - m_use);
+    float p[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2_w(x[i] - m_use);
+      psum += p[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {
+      if (q4 == 0) s_alpha[wave][n16] = alpha;
+      const f4_t ar = *reinterpret_cast<const f4_t *>(&s_alpha[wave][4 * q4]);
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) acc[jt] *= ar;
+    }
+    s4_t phi, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 hi = (__bf16)p[i];
+      phi[i] = __builtin_bit_cast(short, hi);
+      plo[i] = __builtin_bit_cast(short, (__bf16)(p[i] - (float)hi));
+    }
+    // tokens at or past lim may hold any bits (NaN): zero them in the V operand
+    const uint32_t keep_lo = (4 * q4 + 0 < lim ? 0x0000FFFFu : 0u) | (4 * q4 + 1 < lim ? 0xFFFF0000u : 0u);
+    const uint32_t keep_hi = (4 * q4 + 2 < lim ? 0x0000FFFFu : 0u) | (4 * q4 + 3 < lim ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) {
+      const uint32_t w0 = vb[jt >> 1][(jt & 1) * 2] & keep_lo;
+      const uint32_t w1 = vb[jt >> 1][(jt & 1) * 2 + 1] & keep_hi;
+      const s4_t bv = __builtin_bit_cast(s4_t, u2_t{w0, w1});
+      acc[jt] = mfma16_bf16(phi, bv, acc[jt]);
+      acc[jt] = mfma16_bf16(plo, bv, acc[jt]);
+    }
+    if (un < n_units) load(vb, a.vc, pgn);
+  }
+  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc);
+}
+
 // ------------------------------------------------------------------ decode: merge
 //
-// Workgroup (64-channel chunk, query head, sequence) of 4 wavefronts; wave w takes splits
-// w, w+4, ...  M = max_j m_j over the splits that hold pages; w_j = 2^(m_j - M);
+// Workgroup (64-channel chunk, query head, sequence) of 16 wavefronts; wave w takes splits
+// w, w+16, ...  M = max_j m_j over the splits that hold pages; w_j = 2^(m_j - M);
 // out = sum_j w_j o_j / sum_j w_j l_j; lse = ln 2 * (M + log2 sum_j w_j l_j).
+constexpr int kMergeWaves = 16;
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int NCH = D / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
   const int chunk = blockIdx.x % NCH;
   const int hq = (blockIdx.x / NCH) % a.Hq;
   const int s = blockIdx.x / (NCH * a.Hq);
-  int L = a.context_lens[s];
-  L = max(0, min(L, a.max_context_len));
+  const int L = max(0, min(a.context_lens[s], a.max_context_len));
   const int P = (L + kPage - 1) / kPage;
   const int nsa = min(a.NS, (P + a.cpp - 1) / a.cpp);
   const int c = chunk * 64 + lane;
@@ -494,22 +663,28 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float o = 0.0f, l = 0.0f;
-  for (int jj = wave; jj < nsa; jj += 4) {
+#pragma unroll 4
+  for (int jj = wave; jj < nsa; jj += kMergeWaves) {
     const float2 ml = a.ml[base + jj];
+    const float v = a.o_part[(base + jj) * D + c];
     if (ml.x != -INFINITY) {
       const float w = exp2f(ml.x - M);
-      o = fmaf(w, a.o_part[(base + jj) * D + c], o);
+      o = fmaf(w, v, o);
       l = fmaf(w, ml.y, l);
     }
   }
-  __shared__ float s_o[4][64];
-  __shared__ float s_l[4];
+  __shared__ float s_o[kMergeWaves][64];
+  __shared__ float s_l[kMergeWaves];
   s_o[wave][lane] = o;
   if (lane == 0) s_l[wave] = l;
   __syncthreads();
   if (wave == 0) {
-    const float ot = s_o[0][lane] + s_o[1][lane] + s_o[2][lane] + s_o[3][lane];
-    const float lt = s_l[0] + s_l[1] + s_l[2] + s_l[3];
+    float ot = 0.0f, lt = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) {
+      ot += s_o[w][lane];
+      lt += s_l[w];
+    }
     a.out[orow * D + c] = ot / lt;
     if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = kLn2 * (M + log2f(lt));
   }
@@ -536,7 +711,10 @@ template <int D, int NW, bool I8>
 static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
   const size_t smem = NW > 1 ? (size_t)(NW * a.G * D + NW * 32) * sizeof(float) : 0;
-  hipLaunchKernelGGL((decode_split_kernel<D, NW, I8>), dim3(grid), dim3(NW * 64), smem, stream, a);
+  if constexpr (I8)
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a);
+  else
+    hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a);
 }
 
 template <int D, bool I8>
@@ -549,7 +727,7 @@ static void launch_split_nw(const DecodeArgs &a, hipStream_t stream) {
   }
 }
 
-hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t stream) {
   if (dtype == 0) {
     if (a.D == 256) launch_split_nw<256, true>(a, stream);
     else launch_split_nw<128, true>(a, stream);
@@ -557,11 +735,13 @@ hipError_t launch_decode(int dtype, const DecodeArgs &a, hipStream_t stream) {
     if (a.D == 256) launch_split_nw<256, false>(a, stream);
     else launch_split_nw<128, false>(a, stream);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hq * (a.D / 64));
-  if (a.D == 256) hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+  if (a.D == 256) hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, a);
+  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 

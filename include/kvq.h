@@ -109,10 +109,11 @@ int kvq_write(const kvq_cache_t *cache, const void *k, const void *v, const int3
               int32_t num_tokens, void *stream);
 
 /*
- * Bytes of workspace kvq_decode_attention needs for these sizes (num_splits 0 = the
- * automatic choice for max_context_len given to kvq_choose_num_splits).  The workspace holds
- * the split partials: fp32 weighted sums [S][Hq][splits][D] and (max, sum) pairs
- * [S][Hq][splits][2].  Returns 0 on invalid arguments.
+ * Bytes of workspace kvq_decode_attention needs for these sizes; num_splits is the split
+ * count actually used (1..4096; for the automatic choice pass kvq_choose_num_splits()'s
+ * result).  The workspace holds the split partials: fp32 weighted sums [S][Hq][splits][D]
+ * (256-byte aligned) followed by (max, sum) pairs [S][Hq][splits][2].  Returns 0 on invalid
+ * arguments.
  */
 size_t kvq_decode_workspace_bytes(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_splits);
@@ -146,6 +147,24 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two halves of kvq_decode_attention, for callers that combine partials themselves
+ * (for instance partials of one sequence computed in several places) or time the split
+ * kernel alone.  kvq_decode_partials writes, for every split that holds pages, the
+ * unnormalised weighted value sum and its (max, sum) normalisation terms into the workspace
+ * (long-context page, section "Give more GPU workers a piece of the attention calculation");
+ * kvq_decode_merge combines them with those terms into out and lse.  Both take the same
+ * sizes as kvq_decode_attention and must agree on num_splits (0 resolves the same way in
+ * both) and max_context_len.
+ */
+int kvq_decode_partials(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, void *workspace,
+                        size_t workspace_bytes, void *stream);
+int kvq_decode_merge(const kvq_cache_t *cache, const int32_t *context_lens, int32_t max_context_len,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, const void *workspace,
+                     size_t workspace_bytes, float *out, float *lse, void *stream);
 
 /*
  * Checked mode (tests and debugging; not for hot loops).  Copies the metadata (and the bf16

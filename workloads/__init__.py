@@ -209,3 +209,47 @@ def algorithmic_bytes_int8(lens, num_kv_heads: int, head_dim: int) -> int:
 
 def algorithmic_bytes_bf16(lens, num_kv_heads: int, head_dim: int) -> int:
     return int(np.sum(lens, dtype=np.int64)) * num_kv_heads * 4 * head_dim
+
+
+def make_layer_device(cid: int, layer: int = 0, device="cuda", *, aligned: bool = False,
+                      outlier_scale: float = 20.0, num_outliers: int = 4, spare: float = 0.10):
+    """The same recipe as make_layer, with the K/V/Q draws made by torch on the device (seeded
+    torch.Generator) so that multi-gigabyte benchmark inputs need no host round trip.  Block
+    tables, context lengths, slots and outlier channels come from the numpy streams of
+    make_layer.  Returns (Layer with k/v/q set to None, dict of device tensors k, v, q as bf16)."""
+    import torch
+
+    cfg = CONFIGS[cid]
+    lens = context_lens_for(cfg)
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    S = lens.shape[0]
+    bt, nb, used = block_tables_for(cfg, lens, _rng(cid, layer, 1), spare)
+    total = int(lens.sum())
+    token_seq = np.repeat(np.arange(S, dtype=np.int32), lens)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    token_pos = (np.arange(total, dtype=np.int64) - np.repeat(starts, lens)).astype(np.int32)
+    slots = bt[token_seq, token_pos // PAGE].astype(np.int64) * PAGE + token_pos % PAGE
+    g_out = _rng(cid, layer, 2)
+    kv_out = np.stack([g_out.choice(D, num_outliers, replace=False) for _ in range(Hkv)])
+    G = Hq // Hkv
+    q_out = np.stack([kv_out[h // G] for h in range(Hq)]) if aligned else \
+        np.stack([g_out.choice(D, num_outliers, replace=False) for _ in range(Hq)])
+    mult_kv = torch.ones((Hkv, D), dtype=torch.float32)
+    for h in range(Hkv):
+        mult_kv[h, torch.from_numpy(kv_out[h])] = outlier_scale
+    mult_q = torch.ones((Hq, D), dtype=torch.float32)
+    for h in range(Hq):
+        mult_q[h, torch.from_numpy(q_out[h])] = outlier_scale
+    mult_kv, mult_q = mult_kv.to(device), mult_q.to(device)
+    gen = torch.Generator(device=device)
+    out = {}
+    for name, shape, mult, stream in (("k", (total, Hkv, D), mult_kv, 3), ("v", (total, Hkv, D), mult_kv, 4),
+                                      ("q", (S, Hq, D), mult_q, 5)):
+        gen.manual_seed(int(np.random.SeedSequence([cid, layer, stream]).generate_state(1)[0]))
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        x.mul_(mult)
+        out[name] = x.to(torch.bfloat16)  # round to nearest even
+        del x
+    lay = Layer(cfg, layer, lens, bt, nb, used.astype(np.int32), None, None, None, token_seq, token_pos,
+                slots.astype(np.int32), {"kv_outliers": kv_out, "q_outliers": q_out})
+    return lay, out
