@@ -226,9 +226,10 @@ __device__ __forceinline__ float rows_sum(float x) {
 __device__ __forceinline__ float exp2_w(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Buffer resource of one page or scale tile: loads past `bytes` return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void *base, int64_t index, int bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void *base, int64_t index, int bytes,
+                                                          int valid_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(static_cast<const char *>(base)) + index * bytes, 0,
-                                           bytes, 0x00020000);
+                                           valid_bytes, 0x00020000);
 }
 
 __device__ __forceinline__ u4_t ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -236,13 +237,15 @@ __device__ __forceinline__ u4_t ld16(__amdgpu_buffer_rsrc_t r, int voff, int sof
 }
 
 // Q operand (B of Q.K): lane holds head n16 (zero when n16 >= G), channels 32g + 8*q4 + 0..7.
+// One buffer resource spans the G query rows of the group; lanes of padding heads fall past
+// its end and read zeros, so the loads are unconditional (no divergent branches).
 template <int D>
-__device__ __forceinline__ void load_q(const DecodeArgs &a, int s, int h, int n16, int q4, bool head_ok,
-                                       u4_t (&qraw)[D / 32]) {
-  const uint16_t *qrow = a.q + ((int64_t)s * a.Hq + h * a.G + (head_ok ? n16 : 0)) * D;
+__device__ __forceinline__ void load_q(const DecodeArgs &a, int s, int h, int n16, int q4, u4_t (&qraw)[D / 32]) {
+  const uint16_t *rows = a.q + ((int64_t)s * a.Hq + (int64_t)h * a.G) * D;
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(rows), 0, a.G * D * 2, 0x00020000);
+  const int off = (n16 * D + 8 * q4) * 2;
 #pragma unroll
-  for (int g = 0; g < D / 32; ++g)
-    qraw[g] = head_ok ? *reinterpret_cast<const u4_t *>(qrow + kGroup * g + 8 * q4) : u4_t{0u, 0u, 0u, 0u};
+  for (int g = 0; g < D / 32; ++g) qraw[g] = ld16(r, off, g * kGroup * 2);
 }
 
 // Writes the partial of this wavefront (NW == 1) or of the whole workgroup (LDS merge).
@@ -331,12 +334,73 @@ void decode_split_i8_kernel(DecodeArgs a) {
   const int n_units = (p1 - p0 + 1) >> 1;
   const bool head_ok = n16 < a.G;
 
+  float m_run = -INFINITY, l_run = 0.0f;
+  f4_t acc[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
+  const int voff = lane * 16;  // byte offset of this lane's 16-byte fragment in each KiB of a page
+  auto page_index = [&](int p) -> int64_t {  // (block, head) page of logical page p, block id clamped
+    const int b = min(max(btrow[p], 0), a.NB - 1);
+    return (int64_t)b * a.Hkv + h;
+  };
+  u4_t kb[2][NL], vb[2][NL];
+  uint32_t ksb[2], vsb[2];
+  // Loads are issued unconditionally; for a unit past the end the resources have size 0, so
+  // the loads return zeros without touching memory (and leave no divergent branch behind).
+  auto load_k = [&](int64_t pga, int64_t pgb, bool ok) {
+    const int pb = ok ? PAGE_B : 0, sb = ok ? SCALE_B : 0;
+    const auto ra = page_rsrc(a.kc, pga, PAGE_B, pb), rb = page_rsrc(a.kc, pgb, PAGE_B, pb);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      kb[0][i] = ld16(ra, voff, 1024 * i);
+      kb[1][i] = ld16(rb, voff, 1024 * i);
+    }
+    ksb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pga, SCALE_B, sb), lane * 4, 0, 0);
+    ksb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pgb, SCALE_B, sb), lane * 4, 0, 0);
+  };
+  auto load_v = [&](int64_t pga, int64_t pgb, bool ok) {
+    const int pb = ok ? PAGE_B : 0, sb = ok ? SCALE_B : 0;
+    const auto ra = page_rsrc(a.vc, pga, PAGE_B, pb), rb = page_rsrc(a.vc, pgb, PAGE_B, pb);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      vb[0][i] = ld16(ra, voff, 1024 * i);
+      vb[1][i] = ld16(rb, voff, 1024 * i);
+    }
+    vsb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pga, SCALE_B, sb), lane * 4, 0, 0);
+    vsb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pgb, SCALE_B, sb), lane * 4, 0, 0);
+  };
+  // Scale tile dword `lane` holds (token lane / (NG/2), groups 2*(lane % (NG/2)) and +1); it is
+  // stored transposed [group][token] so that a lane later reads its 4 tokens of a group with one
+  // 8-byte read.  Tokens at or past `lim` are stored as 0.
+  auto stage = [&](int slot, uint32_t w, int lim) {
+    if (lane < SCALE_B / 4) {
+      const int t = lane / (NG / 2), g = 2 * (lane % (NG / 2));
+      const bool ok = t < lim;
+      s_sc[wave][slot][g][t] = ok ? (uint16_t)(w & 0xFFFFu) : (uint16_t)0;
+      s_sc[wave][slot][g + 1][t] = ok ? (uint16_t)(w >> 16) : (uint16_t)0;
+    }
+  };
+  auto scales4 = [&](int slot, int g) -> u2_t {
+    return *reinterpret_cast<const u2_t *>(&s_sc[wave][slot][g][4 * q4]);
+  };
+
+  // Q is loaded first: the first unit's K/V loads queue behind it, not the other way round.
+  u4_t qraw[NG];
+  load_q<D>(a, s, h, n16, q4, qraw);
+  int u = wave;
+  {
+    const bool ok = u < n_units;
+    const int pa = ok ? p0 + 2 * u : p0;
+    const int64_t pga = page_index(pa), pgb = page_index(pa + 1 < p1 ? pa + 1 : pa);
+    load_k(pga, pgb, ok);
+    load_v(pga, pgb, ok);
+  }
   // Q: bf16 rescaled by 2^shift per head so that max |q| lies in [2^14, 2^15): exact in f16.
   // Wave 0 converts the operand once into LDS ([group][lane] 16-byte fragments) for all waves.
   int shift = 0;
   {
-    u4_t qraw[NG];
-    load_q<D>(a, s, h, n16, q4, head_ok, qraw);
     float qmax = 0.0f;
 #pragma unroll
     for (int g = 0; g < NG; ++g)
@@ -364,72 +428,14 @@ void decode_split_i8_kernel(DecodeArgs a) {
   }
   const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
 
-  float m_run = -INFINITY, l_run = 0.0f;
-  f4_t acc[NT];
-#pragma unroll
-  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
-  const int voff = lane * 16;  // byte offset of this lane's 16-byte fragment in each KiB of a page
-  auto page_index = [&](int p) -> int64_t {  // (block, head) page of logical page p, block id clamped
-    const int b = min(max(btrow[p], 0), a.NB - 1);
-    return (int64_t)b * a.Hkv + h;
-  };
-  u4_t kb[2][NL], vb[2][NL];
-  uint32_t ksb[2], vsb[2];
-  auto load_k = [&](int64_t pga, int64_t pgb) {
-    const auto ra = page_rsrc(a.kc, pga, PAGE_B), rb = page_rsrc(a.kc, pgb, PAGE_B);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      kb[0][i] = ld16(ra, voff, 1024 * i);
-      kb[1][i] = ld16(rb, voff, 1024 * i);
-    }
-    ksb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pga, SCALE_B), lane * 4, 0, 0);
-    ksb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pgb, SCALE_B), lane * 4, 0, 0);
-  };
-  auto load_v = [&](int64_t pga, int64_t pgb) {
-    const auto ra = page_rsrc(a.vc, pga, PAGE_B), rb = page_rsrc(a.vc, pgb, PAGE_B);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      vb[0][i] = ld16(ra, voff, 1024 * i);
-      vb[1][i] = ld16(rb, voff, 1024 * i);
-    }
-    vsb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pga, SCALE_B), lane * 4, 0, 0);
-    vsb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pgb, SCALE_B), lane * 4, 0, 0);
-  };
-  // Scale tile dword `lane` holds (token lane / (NG/2), groups 2*(lane % (NG/2)) and +1); it is
-  // stored transposed [group][token] so that a lane later reads its 4 tokens of a group with one
-  // 8-byte read.  Tokens at or past `lim` are stored as 0.
-  auto stage = [&](int slot, uint32_t w, int lim) {
-    if (lane < SCALE_B / 4) {
-      const int t = lane / (NG / 2), g = 2 * (lane % (NG / 2));
-      const bool ok = t < lim;
-      s_sc[wave][slot][g][t] = ok ? (uint16_t)(w & 0xFFFFu) : (uint16_t)0;
-      s_sc[wave][slot][g + 1][t] = ok ? (uint16_t)(w >> 16) : (uint16_t)0;
-    }
-  };
-  auto scales4 = [&](int slot, int g) -> u2_t {
-    return *reinterpret_cast<const u2_t *>(&s_sc[wave][slot][g][4 * q4]);
-  };
-
-  int u = wave;
-  if (u < n_units) {
-    const int pa = p0 + 2 * u;
-    const int64_t pga = page_index(pa), pgb = page_index(pa + 1 < p1 ? pa + 1 : pa);
-    load_k(pga, pgb);
-    load_v(pga, pgb);
-  }
   for (; u < n_units; u += NW) {
     const int pa = p0 + 2 * u;
     const int lim_a = min(L - pa * kPage, kPage);                            // valid tokens of page a
     const int lim_b = (pa + 1 < p1) ? min(L - (pa + 1) * kPage, kPage) : 0;  // of page b
     const int un = u + NW;
-    const int pan = p0 + 2 * un;
-    int64_t pga_n = 0, pgb_n = 0;
-    if (un < n_units) {
-      pga_n = page_index(pan);
-      pgb_n = page_index(pan + 1 < p1 ? pan + 1 : pan);
-    }
+    const bool next_ok = un < n_units;
+    const int pan = next_ok ? p0 + 2 * un : p0;
+    const int64_t pga_n = page_index(pan), pgb_n = page_index(pan + 1 < p1 ? pan + 1 : pan);
 
     // ---- Q.K^T for both pages: one MFMA per 32-channel group, then the group's fp16 scale
     stage(0, ksb[0], kPage);
@@ -455,7 +461,7 @@ void decode_split_i8_kernel(DecodeArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (un < n_units) load_k(pga_n, pgb_n);
+    load_k(pga_n, pgb_n, next_ok);
 
     // ---- online softmax over the unit's 32 tokens (base 2)
     float x[8];
@@ -511,7 +517,7 @@ void decode_split_i8_kernel(DecodeArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each group's temporaries short-lived
     }
-    if (un < n_units) load_v(pga_n, pgb_n);
+    load_v(pga_n, pgb_n, next_ok);
   }
   write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc);
 }
@@ -545,7 +551,7 @@ void decode_split_bf16_kernel(DecodeArgs a) {
   const bool head_ok = n16 < a.G;
 
   u4_t qraw[NG];
-  load_q<D>(a, s, h, n16, q4, head_ok, qraw);
+  load_q<D>(a, s, h, n16, q4, qraw);
   b8_t qop[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) qop[g] = __builtin_bit_cast(b8_t, qraw[g]);
@@ -563,26 +569,28 @@ void decode_split_bf16_kernel(DecodeArgs a) {
     return (int64_t)b * a.Hkv + h;
   };
   u4_t kb[NG], vb[NG];
-  auto load = [&](u4_t(&dst)[NG], const void *base, int64_t pg) {
-    const auto r = page_rsrc(base, pg, PAGE_B);
+  auto load = [&](u4_t(&dst)[NG], const void *base, int64_t pg, bool ok) {
+    const auto r = page_rsrc(base, pg, PAGE_B, ok ? PAGE_B : 0);
 #pragma unroll
     for (int i = 0; i < NG; ++i) dst[i] = ld16(r, voff, 1024 * i);
   };
   int u = wave;
-  if (u < n_units) {
-    const int64_t pg = page_index(p0 + u);
-    load(kb, a.kc, pg);
-    load(vb, a.vc, pg);
+  {
+    const bool ok = u < n_units;
+    const int64_t pg = page_index(ok ? p0 + u : p0);
+    load(kb, a.kc, pg, ok);
+    load(vb, a.vc, pg, ok);
   }
   for (; u < n_units; u += NW) {
     const int lim = min(L - (p0 + u) * kPage, kPage);
     const int un = u + NW;
-    const int64_t pgn = un < n_units ? page_index(p0 + un) : 0;
+    const bool next_ok = un < n_units;
+    const int64_t pgn = page_index(next_ok ? p0 + un : p0);
 
     f4_t score = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) score = mfma_bf16(__builtin_bit_cast(b8_t, kb[g]), qop[g], score);
-    if (un < n_units) load(kb, a.kc, pgn);
+    load(kb, a.kc, pgn, next_ok);
 
     float x[4];
 #pragma unroll
@@ -625,7 +633,7 @@ void decode_split_bf16_kernel(DecodeArgs a) {
       acc[jt] = mfma16_bf16(phi, bv, acc[jt]);
       acc[jt] = mfma16_bf16(plo, bv, acc[jt]);
     }
-    if (un < n_units) load(vb, a.vc, pgn);
+    load(vb, a.vc, pgn, next_ok);
   }
   write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc);
 }
