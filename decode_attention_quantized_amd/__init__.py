@@ -88,7 +88,7 @@ class Cache:
     """One layer's paged KV cache pool in device memory (layout of include/kvq.h).
 
     k, v: int8 [num_blocks][Hkv][16*D] (INT8) or bf16 bits as int16 [num_blocks][Hkv][16*D];
-    k_scales, v_scales: fp16 [num_blocks][Hkv][16][D/32] (INT8 only).
+    k_scales, v_scales: fp16 [num_blocks][Hkv][D/32][16] (INT8 only; group-major pages).
     """
 
     def __init__(self, dtype: str, num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda"):
@@ -100,7 +100,7 @@ class Cache:
         if dtype == "int8":
             self.k = torch.empty(shape, dtype=torch.int8, device=device)
             self.v = torch.empty(shape, dtype=torch.int8, device=device)
-            sshape = (num_blocks, num_kv_heads, PAGE, head_dim // 32)
+            sshape = (num_blocks, num_kv_heads, head_dim // 32, PAGE)
             self.k_scales = torch.empty(sshape, dtype=torch.float16, device=device)
             self.v_scales = torch.empty(sshape, dtype=torch.float16, device=device)
         else:

@@ -70,16 +70,38 @@ __device__ __forceinline__ f4_t mfma_bf16(b8_t a, b8_t b, f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// fma(s, b, c) with s the fp16 number in the low / high half of h2 (exact widening; the
+// compiler emits one v_fma_mix_f32).
+__device__ __forceinline__ float fma_h16lo(uint32_t h2, float b, float c) {
+  return fmaf(f16_bits_to_f32(h2 & 0xFFFFu), b, c);
+}
+__device__ __forceinline__ float fma_h16hi(uint32_t h2, float b, float c) { return fmaf(f16_bits_to_f32(h2 >> 16), b, c); }
+
+// Makes the values available at this point of the program (an empty asm that passes them
+// through), so that the compiler cannot defer the work that produces them past later code.
+// Not volatile: it has no side effects and leaves the block-table loads scalar.
+__device__ __forceinline__ void pin4(f4_t &v) {
+  float a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+  asm("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+  v = f4_t{a0, a1, a2, a3};
+}
+
 // Two P' values of one scale group, split for f16 MFMA operands: with s0, s1 the fp16 scales
 // in the low / high half of `s2`, hi = (f16(p0*s0), f16(p1*s1)) and lo = (f16(p0*s0 - hi0),
 // f16(p1*s1 - hi1)); each is one fused multiply-add rounded once to f16 (v_fma_mix{lo,hi}_f16).
 __device__ __forceinline__ void pprime2(float p0, float p1, uint32_t s2, uint32_t &hi, uint32_t &lo) {
+  // One asm block: the first instruction of each pair defines the low half, the second the
+  // high half.  The trailing s_nop gives the two wait states an MFMA that reads hi or lo next
+  // needs after a VALU write (the compiler does not account for writes made inside asm).
+  // hi / lo are early-clobber: they are written while the inputs are still being read.
   uint32_t h, l;
-  // the first instruction of each pair defines the low half, the second the high half
-  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(h) : "v"(p0), "v"(s2));
-  asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(h) : "v"(p1), "v"(s2));
-  asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel_hi:[0,1,1]" : "=v"(l) : "v"(p0), "v"(s2), "v"(h));
-  asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "+v"(l) : "v"(p1), "v"(s2), "v"(h));
+  asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,1,1]\n\t"
+      "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]\n\t"
+      "s_nop 1"
+      : "=&v"(h), "=&v"(l)
+      : "v"(p0), "v"(p1), "v"(s2));
   hi = h;
   lo = l;
 }
@@ -149,13 +171,13 @@ __global__ __launch_bounds__(256) void kv_write_i8_kernel(WriteArgs a) {
       u2_t w = {packed[2 * qq], packed[2 * qq + 1]};
       *reinterpret_cast<u2_t *>(dst + i8_k_offset(off, kGroup * g + 8 * qq)) = w;
     }
-    a.ks[(page * kPage + off) * NG + g] = sbits;
+    a.ks[(page * NG + g) * kPage + off] = sbits;
   } else {
     int8_t *dst = static_cast<int8_t *>(a.vc) + page * (kPage * D);
 #pragma unroll
     for (int i = 0; i < kGroup; ++i)
       dst[i8_v_offset(off, kGroup * g + i)] = (int8_t)((packed[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-    a.vs[(page * kPage + off) * NG + g] = sbits;
+    a.vs[(page * NG + g) * kPage + off] = sbits;
   }
 }
 
@@ -205,6 +227,14 @@ __global__ __launch_bounds__(256) void kv_write_bf16_kernel(WriteArgs a) {
 // x_t = log2(e) * q.k_t / sqrt(D), and l = sum_t 2^(x_t - m).
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4_t mfma16_f16(h4_t a, h4_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Register buffers (pages in flight + the page being processed) of the INT8 split kernel.
+constexpr int kI8Buffers = 2;
 
 // Max / sum over the four lane rows (lanes n, n+16, n+32, n+48) with the gfx950 row swaps.
 __device__ __forceinline__ float rows_max(float x) {
@@ -224,6 +254,9 @@ __device__ __forceinline__ float rows_sum(float x) {
 // 2^x for x <= 0 (softmax weights); results below 2^-126 may flush to zero, which is far
 // below fp32 resolution next to the largest weight (1).
 __device__ __forceinline__ float exp2_w(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// s_waitcnt immediate for vmcnt(n) alone (expcnt and lgkmcnt left at their maxima).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Buffer resource of one page or scale tile: loads past `bytes` return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void *base, int64_t index, int bytes,
@@ -248,10 +281,13 @@ __device__ __forceinline__ void load_q(const DecodeArgs &a, int s, int h, int n1
   for (int g = 0; g < D / 32; ++g) qraw[g] = ld16(r, off, g * kGroup * 2);
 }
 
-// Writes the partial of this wavefront (NW == 1) or of the whole workgroup (LDS merge).
+// Writes the partial of this wavefront (NW == 1) or of the whole workgroup (LDS merge).  For
+// NW > 1, `merge` is LDS scratch holding, per wave w at merge + w * stride floats, that wave's
+// [G][D] accumulator followed by m[16] and l[16]; every wave must be done with its own region.
 template <int D, int NW>
 __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h, int j, int wave, int n16, int q4,
-                                              float m_run, float l_run, const f4_t (&acc)[D / 16]) {
+                                              float m_run, float l_run, const f4_t (&acc)[D / 16], float *merge,
+                                              int stride) {
   constexpr int NT = D / 16;
   const int G = a.G;
   l_run = rows_sum(l_run);
@@ -266,13 +302,10 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
       }
     if (q4 == 0 && n16 < G) a.ml[row0 + (int64_t)n16 * a.NS] = make_float2(m_run, l_run);
   } else {
-    extern __shared__ float smem[];
-    float *s_acc = smem;             // [NW][G][D]
-    float *s_m = smem + NW * G * D;  // [NW][16]
-    float *s_l = s_m + NW * 16;      // [NW][16]
+    float *mine = merge + wave * stride;
     if (q4 == 0) {
-      s_m[wave * 16 + n16] = m_run;
-      s_l[wave * 16 + n16] = l_run;
+      mine[G * D + n16] = m_run;
+      mine[G * D + 16 + n16] = l_run;
     }
     if (4 * q4 < G) {
 #pragma unroll
@@ -280,32 +313,45 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int hh = 4 * q4 + i;
-          if (hh < G) s_acc[(wave * G + hh) * D + 16 * jt + n16] = acc[jt][i];
+          if (hh < G) mine[hh * D + 16 * jt + n16] = acc[jt][i];
         }
+    }
+    __syncthreads();
+    // per head: M = max_w m_w, the weight 2^(m_w - M) of each wave (in place of m_w) and the
+    // merged (M, l); waves without pages (m_w = -inf) get weight 0
+    if (threadIdx.x < G) {
+      const int hh = threadIdx.x;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, merge[w * stride + G * D + hh]);
+      float l = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        float *r = merge + w * stride;
+        const float mw = r[G * D + hh];
+        const float wt = (mw == -INFINITY) ? 0.0f : exp2_w(mw - M);
+        r[G * D + hh] = wt;
+        l = fmaf(wt, r[G * D + 16 + hh], l);
+      }
+      a.ml[row0 + (int64_t)hh * a.NS] = make_float2(M, l);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < G * D; e += NW * 64) {
       const int hh = e / D, c = e - hh * D;
-      float M = -INFINITY;
+      float o = 0.0f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w * 16 + hh]);
-      float o = 0.0f, l = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = s_m[w * 16 + hh];
-        if (mw != -INFINITY) {
-          const float wt = exp2f(mw - M);
-          o = fmaf(wt, s_acc[(w * G + hh) * D + c], o);
-          l = fmaf(wt, s_l[w * 16 + hh], l);
-        }
-      }
+      for (int w = 0; w < NW; ++w) o = fmaf(merge[w * stride + G * D + hh], merge[w * stride + hh * D + c], o);
       a.o_part[(row0 + (int64_t)hh * a.NS) * D + c] = o;
-      if (c == 0) a.ml[row0 + (int64_t)hh * a.NS] = make_float2(M, l);
     }
   }
 }
 
-// ---- INT8 cache: 2-page units, f16 MFMA for both products
+// ---- INT8 cache: 1-page units in a ring of register buffers, f16 MFMA for both products
+//
+// A wave owns pages p0 + wave + k * NW (k = 0, 1, ...) of its split.  Page k lands in register
+// buffer k % NBUF; the page is requested as soon as its buffer has been read out, so while the
+// wave works on one page the next NBUF - 1 are in flight.  Q and the first page's K are
+// requested before anything else.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_i8_kernel(DecodeArgs a) {
@@ -314,11 +360,13 @@ void decode_split_i8_kernel(DecodeArgs a) {
   constexpr int NL = D / 64;          // 16-byte code loads per lane per page
   constexpr int PAGE_B = kPage * D;   // bytes of one code page
   constexpr int SCALE_B = kPage * NG * 2;  // bytes of one scale tile (= D)
-  __shared__ __attribute__((aligned(16))) h8_t s_q[NG][64];              // Q operand fragments
-  __shared__ __attribute__((aligned(16))) uint16_t s_sc[NW][4][NG][16];  // [wave][Ka,Kb,Va,Vb][group][token]
-  __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];
+  constexpr int NBUF = kI8Buffers;
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[NW][2][SCALE_B / 4];  // K, V scale tiles (group-major)
+  __shared__ __attribute__((aligned(16))) h8_t s_q[NG][64];                   // Q operand fragments
+  __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];              // rescale factors, per head
+  extern __shared__ float s_merge[];                                          // [NW][G*D + 32] (dynamic)
 
-  const int32_t *__restrict__ block_tables = a.block_tables;  // read-only: scalar loads
+  const int32_t *__restrict__ block_tables = a.block_tables;
   const int32_t *__restrict__ context_lens = a.context_lens;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
@@ -331,74 +379,50 @@ void decode_split_i8_kernel(DecodeArgs a) {
   const int p0 = j * a.cpp;
   const int p1 = min(p0 + a.cpp, P);
   if (p0 >= p1) return;  // empty split: nothing written, the merge skips it
-  const int n_units = (p1 - p0 + 1) >> 1;
-  const bool head_ok = n16 < a.G;
-
-  float m_run = -INFINITY, l_run = 0.0f;
-  f4_t acc[NT];
-#pragma unroll
-  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int n_units = p1 - p0;
 
   const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
   const int voff = lane * 16;  // byte offset of this lane's 16-byte fragment in each KiB of a page
-  auto page_index = [&](int p) -> int64_t {  // (block, head) page of logical page p, block id clamped
-    const int b = min(max(btrow[p], 0), a.NB - 1);
-    return (int64_t)b * a.Hkv + h;
-  };
-  u4_t kb[2][NL], vb[2][NL];
-  uint32_t ksb[2], vsb[2];
-  // Loads are issued unconditionally; for a unit past the end the resources have size 0, so
-  // the loads return zeros without touching memory (and leave no divergent branch behind).
-  auto load_k = [&](int64_t pga, int64_t pgb, bool ok) {
-    const int pb = ok ? PAGE_B : 0, sb = ok ? SCALE_B : 0;
-    const auto ra = page_rsrc(a.kc, pga, PAGE_B, pb), rb = page_rsrc(a.kc, pgb, PAGE_B, pb);
+
+  // Block id of page k of the wave: a scalar load (the block table is only read here), issued
+  // one page ahead of its use so that its latency hides behind a page's work.
+  auto block_of = [&](int k) -> int { return btrow[min(p0 + wave + k * NW, p1 - 1)]; };
+  auto page_of = [&](int blk) -> int64_t { return (int64_t)min(max(blk, 0), a.NB - 1) * a.Hkv + h; };
+
+  // ---- register buffers: K / V codes and the page's K / V scale tiles (one dword per lane).
+  // Past the end of the split the resources have size 0: the loads return zeros without
+  // touching memory, so they are issued unconditionally (no divergent branch, no wait merge).
+  u4_t kb[NBUF][NL], vb[NBUF][NL];
+  uint32_t ksb[NBUF], vsb[NBUF];
+  auto issue_k = [&](int b, int k, int blk) {
+    const bool ok = wave + k * NW < n_units;
+    const int64_t page = page_of(blk);
+    const auto r = page_rsrc(a.kc, page, PAGE_B, ok ? PAGE_B : 0);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      kb[0][i] = ld16(ra, voff, 1024 * i);
-      kb[1][i] = ld16(rb, voff, 1024 * i);
-    }
-    ksb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pga, SCALE_B, sb), lane * 4, 0, 0);
-    ksb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, pgb, SCALE_B, sb), lane * 4, 0, 0);
+    for (int i = 0; i < NL; ++i) kb[b][i] = ld16(r, voff, 1024 * i);
+    ksb[b] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, page, SCALE_B, ok ? SCALE_B : 0), lane * 4, 0, 0);
   };
-  auto load_v = [&](int64_t pga, int64_t pgb, bool ok) {
-    const int pb = ok ? PAGE_B : 0, sb = ok ? SCALE_B : 0;
-    const auto ra = page_rsrc(a.vc, pga, PAGE_B, pb), rb = page_rsrc(a.vc, pgb, PAGE_B, pb);
+  auto issue_v = [&](int b, int k, int blk) {
+    const bool ok = wave + k * NW < n_units;
+    const int64_t page = page_of(blk);
+    const auto r = page_rsrc(a.vc, page, PAGE_B, ok ? PAGE_B : 0);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      vb[0][i] = ld16(ra, voff, 1024 * i);
-      vb[1][i] = ld16(rb, voff, 1024 * i);
-    }
-    vsb[0] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pga, SCALE_B, sb), lane * 4, 0, 0);
-    vsb[1] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, pgb, SCALE_B, sb), lane * 4, 0, 0);
-  };
-  // Scale tile dword `lane` holds (token lane / (NG/2), groups 2*(lane % (NG/2)) and +1); it is
-  // stored transposed [group][token] so that a lane later reads its 4 tokens of a group with one
-  // 8-byte read.  Tokens at or past `lim` are stored as 0.
-  auto stage = [&](int slot, uint32_t w, int lim) {
-    if (lane < SCALE_B / 4) {
-      const int t = lane / (NG / 2), g = 2 * (lane % (NG / 2));
-      const bool ok = t < lim;
-      s_sc[wave][slot][g][t] = ok ? (uint16_t)(w & 0xFFFFu) : (uint16_t)0;
-      s_sc[wave][slot][g + 1][t] = ok ? (uint16_t)(w >> 16) : (uint16_t)0;
-    }
-  };
-  auto scales4 = [&](int slot, int g) -> u2_t {
-    return *reinterpret_cast<const u2_t *>(&s_sc[wave][slot][g][4 * q4]);
+    for (int i = 0; i < NL; ++i) vb[b][i] = ld16(r, voff, 1024 * i);
+    vsb[b] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, page, SCALE_B, ok ? SCALE_B : 0), lane * 4, 0, 0);
   };
 
-  // Q is loaded first: the first unit's K/V loads queue behind it, not the other way round.
+  int blk[NBUF];
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) blk[b] = block_of(b);
   u4_t qraw[NG];
   load_q<D>(a, s, h, n16, q4, qraw);
-  int u = wave;
-  {
-    const bool ok = u < n_units;
-    const int pa = ok ? p0 + 2 * u : p0;
-    const int64_t pga = page_index(pa), pgb = page_index(pa + 1 < p1 ? pa + 1 : pa);
-    load_k(pga, pgb, ok);
-    load_v(pga, pgb, ok);
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  issue_k(0, 0, blk[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
   // Q: bf16 rescaled by 2^shift per head so that max |q| lies in [2^14, 2^15): exact in f16.
-  // Wave 0 converts the operand once into LDS ([group][lane] 16-byte fragments) for all waves.
+  // Every wave derives the per-head shift; wave 0 stores the operand into LDS ([group][lane]
+  // 16-byte fragments) for all waves.
   int shift = 0;
   {
     float qmax = 0.0f;
@@ -424,102 +448,147 @@ void decode_split_i8_kernel(DecodeArgs a) {
         s_q[g][lane] = qg;
       }
     }
-    __syncthreads();
+    // LDS-only fences: __syncthreads would also wait for the page loads in flight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
   const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
+  // (scheduling barriers keep the loads in this order: the compiler's wait counts follow it)
+  issue_v(0, 0, blk[0]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 1; b < NBUF; ++b) {
+    issue_k(b, b, blk[b]);
+    issue_v(b, b, blk[b]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int blk_next = block_of(NBUF);
 
-  for (; u < n_units; u += NW) {
-    const int pa = p0 + 2 * u;
-    const int lim_a = min(L - pa * kPage, kPage);                            // valid tokens of page a
-    const int lim_b = (pa + 1 < p1) ? min(L - (pa + 1) * kPage, kPage) : 0;  // of page b
-    const int un = u + NW;
-    const bool next_ok = un < n_units;
-    const int pan = next_ok ? p0 + 2 * un : p0;
-    const int64_t pga_n = page_index(pan), pgb_n = page_index(pan + 1 < p1 ? pan + 1 : pan);
+  float m_run = -INFINITY, l_run = 0.0f;
+  f4_t acc[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // the Q operand stays in registers for the whole split
+  h8_t qop[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) qop[g] = s_q[g][lane];
+  // Scale tiles are restaged token-quad-major ([q4][group][4 tokens]) so that a lane reads the
+  // scales of its 4 tokens for all groups with 8*NG contiguous bytes.  Tile dword l (group-major
+  // [group][token]) holds group l / 8, tokens 2 (l % 8) and 2 (l % 8) + 1.
+  const int st_dw = (((lane & 7) >> 1) * NG + (lane >> 3)) * 2 + (lane & 1);  // restaged dword of dword l
+  auto stage = [&](int which, uint32_t w) {
+    if (lane < SCALE_B / 4) s_sc[wave][which][st_dw] = w;
+  };
+  auto scales = [&](int which, u2_t (&out)[NG]) {
+    const u4_t *src = reinterpret_cast<const u4_t *>(&s_sc[wave][which][q4 * NG * 2]);
+#pragma unroll
+    for (int i = 0; i < NG / 2; ++i) {
+      const u4_t w = src[i];
+      out[2 * i] = u2_t{w[0], w[1]};
+      out[2 * i + 1] = u2_t{w[2], w[3]};
+    }
+  };
 
-    // ---- Q.K^T for both pages: one MFMA per 32-channel group, then the group's fp16 scale
-    stage(0, ksb[0], kPage);
-    stage(1, ksb[1], kPage);
-    f4_t sc[2] = {f4_t{0.0f, 0.0f, 0.0f, 0.0f}, f4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-    // Q fragments are re-read from LDS every unit rather than kept in 32 registers (a volatile
-    // LDS read, so that the compiler does not hoist these loop-invariant loads).
-    const volatile __attribute__((address_space(3))) h8_t *qlds =
-        (const volatile __attribute__((address_space(3))) h8_t *)(&s_q[0][0]);
+  // One page from buffer b: Q.K^T, one online-softmax update, P.V.
+  auto process = [&](int b, int k) {
+    const int u = wave + k * NW;  // (past the split's last page: no valid token)
+    const int lim = u < n_units ? min(L - (p0 + u) * kPage, kPage) : 0;  // valid tokens of the page
+    stage(0, ksb[b]);
+    u2_t ksc[NG];
+    scales(0, ksc);
+    // ---- Q.K^T: one MFMA per 32-channel group, then the group's fp16 scale
+    // one MFMA per group; the scale step of group g runs after group g + 1's MFMA is issued
+    f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto qk_group = [&](int g) -> f4_t {
+      return mfma_f16(i8x8_to_h8(kb[b][g >> 1][(g & 1) * 2], kb[b][g >> 1][(g & 1) * 2 + 1]), qop[g],
+                      f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+    };
+    auto scale_group = [&](int g, const f4_t &c) {
+      const u2_t sw = ksc[g];
+      sc[0] = fma_h16lo(sw[0], c[0], sc[0]);
+      sc[1] = fma_h16hi(sw[0], c[1], sc[1]);
+      sc[2] = fma_h16lo(sw[1], c[2], sc[2]);
+      sc[3] = fma_h16hi(sw[1], c[3], sc[3]);
+      pin4(sc);  // keeps the scale step here (else every group's result stays live)
+    };
+    f4_t c_prev = qk_group(0);
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const h8_t qg = qlds[g * 64 + lane];
-#pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
-        const h8_t av = i8x8_to_h8(kb[pg][g >> 1][(g & 1) * 2], kb[pg][g >> 1][(g & 1) * 2 + 1]);
-        const f4_t c = mfma_f16(av, qg, f4_t{0.0f, 0.0f, 0.0f, 0.0f});
-        const u2_t sw = scales4(pg, g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t hbits = (i & 1) ? (sw[i >> 1] >> 16) : (sw[i >> 1] & 0xFFFFu);
-          sc[pg][i] = fmaf(f16_bits_to_f32(hbits), c[i], sc[pg][i]);
-        }
-      }
+    for (int g = 1; g < NG; ++g) {
+      const f4_t c = qk_group(g);
+      scale_group(g - 1, c_prev);
+      c_prev = c;
       __builtin_amdgcn_sched_barrier(0);
     }
-    load_k(pga_n, pgb_n, next_ok);
-
-    // ---- online softmax over the unit's 32 tokens (base 2)
-    float x[8];
+    scale_group(NG - 1, c_prev);
+    // ---- online softmax over the page's 16 tokens (base 2).  Padding heads (Q = 0) get finite
+    // scores; their rows are never written out.
+    float x[4];
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = head_ok && (4 * q4 + i) < (pg ? lim_b : lim_a);
-        x[4 * pg + i] = ok ? sc[pg][i] * cmul : -INFINITY;
-      }
-    float mx = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim) ? sc[i] * cmul : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = (m_new == m_run) ? 1.0f : exp2_w(m_run - m_use);
-    float p[8];
+    const bool grew = alpha != 1.0f && m_run != -INFINITY;  // (the first update finds acc = 0)
+    float p[4];
     float psum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2_w(x[e] - m_use);
-      psum += p[e];
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2_w(x[i] - m_use);
+      psum += p[i];
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    if (__any(alpha != 1.0f)) {  // some head's maximum grew: rescale its accumulator rows
+    if (__any(grew)) {  // some head's maximum grew: rescale its accumulator rows
       if (q4 == 0) s_alpha[wave][n16] = alpha;
-      const f4_t ar = *reinterpret_cast<const f4_t *>(&s_alpha[wave][4 * q4]);
+      const f4_t ar = *reinterpret_cast<const f4_t *>(&s_alpha[wave][4 * q4]);  // heads 4*q4 .. +3
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) acc[jt] *= ar;
     }
-
-    // ---- P.V: P' = p * s_v per (token, group) as f16 hi + lo, times exact f16 V codes
-    stage(2, vsb[0], lim_a);
-    stage(3, vsb[1], lim_b);
+    // ---- P.V: P' = p * s_v per (token, group) as f16 hi + lo, times exact f16 V codes.  V scales
+    // of tokens past the context are masked to 0 (their codes and scales may be stale).
+    stage(1, vsb[b]);
+    u2_t vsc[NG];
+    scales(1, vsc);
+    const int nv = min(max(lim - 4 * q4, 0), 4);
+    const u2_t msk = {nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0xFFFFu : 0u), nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0xFFFFu : 0u)};
+    // One 16x16x32 MFMA per output tile covers both parts of P': its 32 K-slots are, per lane,
+    // (hi of tokens 4 q4 .. 4 q4 + 3, lo of the same tokens), and the V operand holds the lane's
+    // 4 codes twice.
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const u2_t sa = scales4(2, g), sb = scales4(3, g);
-      uint32_t hw[4], lw[4];
-      pprime2(p[0], p[1], sa[0], hw[0], lw[0]);
-      pprime2(p[2], p[3], sa[1], hw[1], lw[1]);
-      pprime2(p[4], p[5], sb[0], hw[2], lw[2]);
-      pprime2(p[6], p[7], sb[1], hw[3], lw[3]);
-      const h8_t phi = __builtin_bit_cast(h8_t, u4_t{hw[0], hw[1], hw[2], hw[3]});
-      const h8_t plo = __builtin_bit_cast(h8_t, u4_t{lw[0], lw[1], lw[2], lw[3]});
+      const u2_t sv = vsc[g] & msk;
+      uint32_t hw[2], lw[2];
+      pprime2(p[0], p[1], sv[0], hw[0], lw[0]);
+      pprime2(p[2], p[3], sv[1], hw[1], lw[1]);
+      const h8_t pp = __builtin_bit_cast(h8_t, u4_t{hw[0], hw[1], lw[0], lw[1]});
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int jt = 2 * g + jj;
-        const h8_t bv = i8x8_to_h8(vb[0][jt >> 2][jt & 3], vb[1][jt >> 2][jt & 3]);
-        acc[jt] = mfma_f16(phi, bv, acc[jt]);
-        acc[jt] = mfma_f16(plo, bv, acc[jt]);
+        uint32_t v0, v1;
+        i8x4_to_f16(vb[b][jt >> 2][jt & 3], v0, v1);
+        acc[jt] = mfma_f16(pp, __builtin_bit_cast(h8_t, u4_t{v0, v1, v0, v1}), acc[jt]);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each group's temporaries short-lived
     }
-    load_v(pga_n, pgb_n, next_ok);
+  };
+
+  // A uniform trip count and no early exit: pages past the split's end read zeros and are
+  // fully masked (p = 0), which keeps the in-flight buffers in fixed registers across the loop.
+  const int my_units = wave < n_units ? (n_units - wave + NW - 1) / NW : 0;
+  for (int k = 0; k < my_units; k += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      process(b, k + b);
+      issue_k(b, k + b + NBUF, blk_next);
+      issue_v(b, k + b + NBUF, blk_next);
+      __builtin_amdgcn_sched_barrier(0);
+      blk_next = block_of(k + b + NBUF + 1);
+    }
   }
-  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc);
+  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, a.G * D + 32);
 }
 
 // ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
@@ -635,7 +704,8 @@ void decode_split_bf16_kernel(DecodeArgs a) {
     }
     load(vb, a.vc, pgn, next_ok);
   }
-  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc);
+  extern __shared__ float s_merge[];  // [NW][G*D + 32] floats (dynamic)
+  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, a.G * D + 32);
 }
 
 // ------------------------------------------------------------------ decode: merge
@@ -718,7 +788,7 @@ hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream) {
 template <int D, int NW, bool I8>
 static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
-  const size_t smem = NW > 1 ? (size_t)(NW * a.G * D + NW * 32) * sizeof(float) : 0;
+  const size_t smem = NW > 1 ? (size_t)NW * (a.G * D + 32) * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a);
   else

@@ -43,8 +43,9 @@
  *                      K:  ((((c>>6)<<6) | (((c>>3)&3)<<4) | t) << 4) | (((c>>5)&1)<<3) | (c&7)
  *                      V:  ((((c>>6)<<6) | ((t>>2)<<4) | (c&15)) << 4) | (((c>>4)&3)<<2) | (t&3)
  *                    (kvq_page_offset() returns the same values).
- *     k_scales,      binary16, [num_blocks][Hkv][16][D/32]: scale of (token t, group c/32).
- *     v_scales
+ *     k_scales,      binary16, [num_blocks][Hkv][D/32][16]: scale of (token t, group g = c/32)
+ *     v_scales       at element ((b*Hkv + h)*(D/32) + g)*16 + t (group-major within a page, so
+ *                    that the 4 scales of one group a lane needs are 8 contiguous bytes).
  *   BF16 (KVQ_BF16):  k, v bfloat16, pages of 16*D values (2*16*D bytes); element of (t, c):
  *                      K:  (((c>>5)<<6) | (((c>>3)&3)<<4) | t) << 3 | (c&7)
  *                      V:  (((c>>5)<<6) | ((t>>2)<<4) | (c&15)) << 3 | (((c>>4)&1)<<2) | (t&3)

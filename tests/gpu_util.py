@@ -7,7 +7,7 @@ import torch
 
 import decode_attention_quantized_amd as K
 import oracle as O
-from tests.layout import to_logical, to_physical
+from tests.layout import scales_to_logical, scales_to_physical, to_logical, to_physical
 
 # Output tolerance: every element must satisfy |gpu - oracle| <= ATOL + RTOL * |oracle|.
 ATOL, RTOL = 2e-3, 1e-3
@@ -47,8 +47,8 @@ class Pair:
         if self.dtype == "int8":
             kc = to_logical(g.k.cpu().numpy(), "int8", self.D, "k")
             vc = to_logical(g.v.cpu().numpy(), "int8", self.D, "v")
-            ks = g.k_scales.cpu().view(torch.int16).numpy().view(np.uint16)
-            vs = g.v_scales.cpu().view(torch.int16).numpy().view(np.uint16)
+            ks = scales_to_logical(g.k_scales.cpu().view(torch.int16).numpy().view(np.uint16))
+            vs = scales_to_logical(g.v_scales.cpu().view(torch.int16).numpy().view(np.uint16))
             return kc, vc, ks, vs
         kc = to_logical(g.k.cpu().numpy().view(np.uint16), "bf16", self.D, "k")
         vc = to_logical(g.v.cpu().numpy().view(np.uint16), "bf16", self.D, "v")
@@ -72,8 +72,8 @@ class Pair:
         if self.dtype == "int8":
             g.k.copy_(torch.from_numpy(to_physical(o.k, "int8", self.D, "k")))
             g.v.copy_(torch.from_numpy(to_physical(o.v, "int8", self.D, "v")))
-            g.k_scales.view(torch.int16).copy_(torch.from_numpy(o.k_scales.view(np.int16)))
-            g.v_scales.view(torch.int16).copy_(torch.from_numpy(o.v_scales.view(np.int16)))
+            g.k_scales.view(torch.int16).copy_(torch.from_numpy(scales_to_physical(o.k_scales).view(np.int16)))
+            g.v_scales.view(torch.int16).copy_(torch.from_numpy(scales_to_physical(o.v_scales).view(np.int16)))
         else:
             g.k.copy_(torch.from_numpy(to_physical(o.k, "bf16", self.D, "k").view(np.int16)))
             g.v.copy_(torch.from_numpy(to_physical(o.v, "bf16", self.D, "v").view(np.int16)))

@@ -33,3 +33,13 @@ def to_physical(rows: np.ndarray, dtype: str, head_dim: int, which: str) -> np.n
     out = np.empty(rows.shape[:-2] + (PAGE * head_dim,), dtype=rows.dtype)
     out[..., idx] = rows
     return out
+
+
+def scales_to_logical(s: np.ndarray) -> np.ndarray:
+    """[NB][Hkv][D/32][16] device scale pages (group-major) -> [NB][Hkv][16][D/32]."""
+    return np.ascontiguousarray(np.swapaxes(s, -1, -2))
+
+
+def scales_to_physical(s: np.ndarray) -> np.ndarray:
+    """[NB][Hkv][16][D/32] logical scales -> [NB][Hkv][D/32][16] device scale pages."""
+    return np.ascontiguousarray(np.swapaxes(s, -1, -2))
