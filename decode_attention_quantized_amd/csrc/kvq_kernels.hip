@@ -281,15 +281,22 @@ __device__ __forceinline__ void load_q(const DecodeArgs &a, int s, int h, int n1
   for (int g = 0; g < D / 32; ++g) qraw[g] = ld16(r, off, g * kGroup * 2);
 }
 
-// Writes the partial of this wavefront (NW == 1) or of the whole workgroup (LDS merge).  For
-// NW > 1, `merge` is LDS scratch holding, per wave w at merge + w * stride floats, that wave's
-// [G][D] accumulator followed by m[16] and l[16]; every wave must be done with its own region.
+// Merge scratch of one wave (floats): its accumulator tiles as [tile][lane][4], then m[16]
+// and l[16].
+template <int D>
+constexpr int merge_stride() { return (D / 16) * 256 + 32; }
+
+// Writes the partial of this wavefront (NW == 1) or of the whole workgroup (NW > 1: an LDS
+// merge; `merge` holds NW regions of merge_stride<D>() floats).  Every wave stores its
+// accumulator tiles as they sit in its registers; wave w then combines tiles w, w + NW, ...
+// of all waves for its own lanes' rows, each wave's rows weighted by 2^(m_w - M).
 template <int D, int NW>
 __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h, int j, int wave, int n16, int q4,
-                                              float m_run, float l_run, const f4_t (&acc)[D / 16], float *merge,
-                                              int stride) {
+                                              float m_run, float l_run, const f4_t (&acc)[D / 16], float *merge) {
   constexpr int NT = D / 16;
+  constexpr int ST = merge_stride<D>();
   const int G = a.G;
+  const int lane = q4 * 16 + n16;
   l_run = rows_sum(l_run);
   const int64_t row0 = ((int64_t)s * a.Hq + (int64_t)h * G) * a.NS + j;  // partial of head h*G + 0
   if constexpr (NW == 1) {
@@ -302,46 +309,54 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
       }
     if (q4 == 0 && n16 < G) a.ml[row0 + (int64_t)n16 * a.NS] = make_float2(m_run, l_run);
   } else {
-    float *mine = merge + wave * stride;
-    if (q4 == 0) {
-      mine[G * D + n16] = m_run;
-      mine[G * D + 16 + n16] = l_run;
+    float *mine = merge + wave * ST;
+    if (4 * q4 < G) {  // lanes that hold a real head
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) *reinterpret_cast<f4_t *>(mine + (jt * 64 + lane) * 4) = acc[jt];
     }
-    if (4 * q4 < G) {
-#pragma unroll
-      for (int jt = 0; jt < NT; ++jt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int hh = 4 * q4 + i;
-          if (hh < G) mine[hh * D + 16 * jt + n16] = acc[jt][i];
-        }
+    if (q4 == 0) {
+      mine[NT * 256 + n16] = m_run;
+      mine[NT * 256 + 16 + n16] = l_run;
     }
     __syncthreads();
-    // per head: M = max_w m_w, the weight 2^(m_w - M) of each wave (in place of m_w) and the
-    // merged (M, l); waves without pages (m_w = -inf) get weight 0
-    if (threadIdx.x < G) {
-      const int hh = threadIdx.x;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, merge[w * stride + G * D + hh]);
-      float l = 0.0f;
+    if (4 * q4 < G) {
+      // weights of every wave for this lane's rows (heads 4 q4 .. 4 q4 + 3)
+      f4_t mw[NW], wt[NW];
+      f4_t M = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        float *r = merge + w * stride;
-        const float mw = r[G * D + hh];
-        const float wt = (mw == -INFINITY) ? 0.0f : exp2_w(mw - M);
-        r[G * D + hh] = wt;
-        l = fmaf(wt, r[G * D + 16 + hh], l);
-      }
-      a.ml[row0 + (int64_t)hh * a.NS] = make_float2(M, l);
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < G * D; e += NW * 64) {
-      const int hh = e / D, c = e - hh * D;
-      float o = 0.0f;
+        mw[w] = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 4 * q4);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) o = fmaf(merge[w * stride + G * D + hh], merge[w * stride + hh * D + c], o);
-      a.o_part[(row0 + (int64_t)hh * a.NS) * D + c] = o;
+        for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], mw[w][i]);
+      }
+      f4_t Lsum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const f4_t lw = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 16 + 4 * q4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wt[w][i] = (mw[w][i] == -INFINITY) ? 0.0f : exp2_w(mw[w][i] - M[i]);  // waves without pages: 0
+          Lsum[i] = fmaf(wt[w][i], lw[i], Lsum[i]);
+        }
+      }
+      if (wave == 0 && n16 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * q4 + i < G) a.ml[row0 + (int64_t)(4 * q4 + i) * a.NS] = make_float2(M[i], Lsum[i]);
+      }
+#pragma unroll
+      for (int jt = wave; jt < NT; jt += NW) {
+        f4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const f4_t v = *reinterpret_cast<const f4_t *>(merge + w * ST + (jt * 64 + lane) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = fmaf(wt[w][i], v[i], o[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * q4 + i < G) a.o_part[(row0 + (int64_t)(4 * q4 + i) * a.NS) * D + 16 * jt + n16] = o[i];
+      }
     }
   }
 }
@@ -557,13 +572,23 @@ void decode_split_i8_kernel(DecodeArgs a) {
     // One 16x16x32 MFMA per output tile covers both parts of P': its 32 K-slots are, per lane,
     // (hi of tokens 4 q4 .. 4 q4 + 3, lo of the same tokens), and the V operand holds the lane's
     // 4 codes twice.
+    // P' = p * s_v as f16 hi + lo with packed f16 arithmetic, two tokens per instruction:
+    // p = ph + pl (f16 hi / lo of p, once per page), hi = f16(ph * s), lo = f16(pl * s + r) with
+    // r = ph * s - hi exact (a fused multiply-add); hi + lo is within about 2^-21 of p * s.
+    const h2_t ph01 = {(_Float16)p[0], (_Float16)p[1]}, ph23 = {(_Float16)p[2], (_Float16)p[3]};
+    const h2_t pl01 = {(_Float16)(p[0] - (float)ph01[0]), (_Float16)(p[1] - (float)ph01[1])};
+    const h2_t pl23 = {(_Float16)(p[2] - (float)ph23[0]), (_Float16)(p[3] - (float)ph23[1])};
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const u2_t sv = vsc[g] & msk;
-      uint32_t hw[2], lw[2];
-      pprime2(p[0], p[1], sv[0], hw[0], lw[0]);
-      pprime2(p[2], p[3], sv[1], hw[1], lw[1]);
-      const h8_t pp = __builtin_bit_cast(h8_t, u4_t{hw[0], hw[1], lw[0], lw[1]});
+      // (through scalars: a bit cast of a vector element subscript reads the wrong element)
+      const uint32_t w01 = sv[0], w23 = sv[1];
+      const h2_t s01 = __builtin_bit_cast(h2_t, w01), s23 = __builtin_bit_cast(h2_t, w23);
+      const h2_t hi01 = ph01 * s01, hi23 = ph23 * s23;
+      const h2_t lo01 = __builtin_elementwise_fma(pl01, s01, __builtin_elementwise_fma(ph01, s01, -hi01));
+      const h2_t lo23 = __builtin_elementwise_fma(pl23, s23, __builtin_elementwise_fma(ph23, s23, -hi23));
+      const h8_t pp = __builtin_bit_cast(h8_t, u4_t{__builtin_bit_cast(uint32_t, hi01), __builtin_bit_cast(uint32_t, hi23),
+                                                   __builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int jt = 2 * g + jj;
@@ -588,7 +613,7 @@ void decode_split_i8_kernel(DecodeArgs a) {
       blk_next = block_of(k + b + NBUF + 1);
     }
   }
-  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, a.G * D + 32);
+  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge);
 }
 
 // ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
@@ -615,7 +640,7 @@ void decode_split_bf16_kernel(DecodeArgs a) {
   const int P = (L + kPage - 1) / kPage;
   const int p0 = j * a.cpp;
   const int p1 = min(p0 + a.cpp, P);
-  if (p0 >= p1) return;
+  if (p0 >= p1) return;  // empty split: nothing written, the merge skips it
   const int n_units = p1 - p0;
   const bool head_ok = n16 < a.G;
 
@@ -705,66 +730,82 @@ void decode_split_bf16_kernel(DecodeArgs a) {
     load(vb, a.vc, pgn, next_ok);
   }
   extern __shared__ float s_merge[];  // [NW][G*D + 32] floats (dynamic)
-  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, a.G * D + 32);
+  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge);
 }
 
 // ------------------------------------------------------------------ decode: merge
 //
-// Workgroup (64-channel chunk, query head, sequence) of 16 wavefronts; wave w takes splits
-// w, w+16, ...  M = max_j m_j over the splits that hold pages; w_j = 2^(m_j - M);
-// out = sum_j w_j o_j / sum_j w_j l_j; lse = ln 2 * (M + log2 sum_j w_j l_j).
-constexpr int kMergeWaves = 16;
+// Workgroup (64-channel chunk, query head, sequence) of kMergeWaves wavefronts; wave w takes
+// splits w, w + kMergeWaves, ... and folds them into a running (m, l, o) with the same rescaling
+// as the online softmax, so the partials are read in one pass (no separate pass for the global
+// maximum).  Only the splits that hold pages are folded (their count follows from the context
+// length, which is read alongside the first partials).  The waves' results are then folded the
+// same way through LDS:  out = o / l;  lse = ln 2 * (m + log2 l).
+constexpr int kMergeWaves = 4;
 
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int NCH = D / 64;
+  constexpr int UNR = 8;  // partials requested together per wave
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunk = blockIdx.x % NCH;
   const int hq = (blockIdx.x / NCH) % a.Hq;
   const int s = blockIdx.x / (NCH * a.Hq);
-  const int L = max(0, min(a.context_lens[s], a.max_context_len));
-  const int P = (L + kPage - 1) / kPage;
-  const int nsa = min(a.NS, (P + a.cpp - 1) / a.cpp);
   const int c = chunk * 64 + lane;
   const int64_t orow = ((int64_t)s * a.Hq + hq);
-  if (nsa == 0) {
-    if (wave == 0) {
-      a.out[orow * D + c] = 0.0f;
-      if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = -INFINITY;
-    }
-    return;
-  }
   const int64_t base = orow * a.NS;
-  float M = -INFINITY;
-  for (int jj = lane; jj < nsa; jj += 64) M = fmaxf(M, a.ml[base + jj].x);
+
+  const int Lc = a.context_lens[s];  // (the loads below do not depend on it)
+  float m = -INFINITY, l = 0.0f, o = 0.0f;
+  auto fold = [&](float mj, float lj, float oj) {
+    if (mj == -INFINITY) return;
+    const float mn = fmaxf(m, mj);
+    const float a0 = exp2_w(m - mn), a1 = exp2_w(mj - mn);  // (m = -inf gives a0 = 0)
+    o = fmaf(o, a0, oj * a1);
+    l = fmaf(l, a0, lj * a1);
+    m = mn;
+  };
+  // buffer loads over this head's partials: vector loads (a uniform address would otherwise
+  // become a scalar load waited on one at a time)
+  const auto rml = __builtin_amdgcn_make_buffer_rsrc(a.ml + base, 0, a.NS * 8, 0x00020000);
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc(a.o_part + base * D, 0, a.NS * D * 4, 0x00020000);
+  for (int j0 = wave; j0 < a.NS; j0 += kMergeWaves * UNR) {
+    float2 mlv[UNR];
+    float ov[UNR];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float o = 0.0f, l = 0.0f;
-#pragma unroll 4
-  for (int jj = wave; jj < nsa; jj += kMergeWaves) {
-    const float2 ml = a.ml[base + jj];
-    const float v = a.o_part[(base + jj) * D + c];
-    if (ml.x != -INFINITY) {
-      const float w = exp2f(ml.x - M);
-      o = fmaf(w, v, o);
-      l = fmaf(w, ml.y, l);
+    for (int u = 0; u < UNR; ++u) {
+      const int jj = j0 + u * kMergeWaves;  // (past NS: the resources return 0; skipped below)
+      const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, 0, jj * 8, 0));
+      mlv[u] = make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+      ov[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, c * 4, jj * D * 4, 0));
     }
+    const int L = max(0, min(Lc, a.max_context_len));
+    const int nsa = min(a.NS, ((L + kPage - 1) / kPage + a.cpp - 1) / a.cpp);  // splits with pages
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (j0 + u * kMergeWaves < nsa) fold(mlv[u].x, mlv[u].y, ov[u]);
   }
-  __shared__ float s_o[kMergeWaves][64];
-  __shared__ float s_l[kMergeWaves];
+  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves], s_o[kMergeWaves][64];
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_l[wave] = l;
+  }
   s_o[wave][lane] = o;
-  if (lane == 0) s_l[wave] = l;
   __syncthreads();
   if (wave == 0) {
-    float ot = 0.0f, lt = 0.0f;
+    m = -INFINITY;
+    l = 0.0f;
+    o = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) {
-      ot += s_o[w][lane];
-      lt += s_l[w];
+    for (int w = 0; w < kMergeWaves; ++w) fold(s_m[w], s_l[w], s_o[w][lane]);
+    if (m == -INFINITY) {  // no split holds a page: empty context
+      a.out[orow * D + c] = 0.0f;
+      if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = -INFINITY;
+    } else {
+      a.out[orow * D + c] = o / l;
+      if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = kLn2 * (m + log2f(l));
     }
-    a.out[orow * D + c] = ot / lt;
-    if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = kLn2 * (M + log2f(lt));
   }
 }
 
@@ -788,7 +829,7 @@ hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream) {
 template <int D, int NW, bool I8>
 static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
-  const size_t smem = NW > 1 ? (size_t)NW * (a.G * D + 32) * sizeof(float) : 0;  // merge scratch
+  const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a);
   else
