@@ -9,10 +9,13 @@ the whole multi-layer cache from HBM (1.06 GiB of INT8 K/V at 32K context, far a
 value distribution, resident in HBM before the timed region.
 
 Timing: the step is captured once into a HIP graph and replayed; HIP events bracket the
-timed replays.  The decode_split kernel is also timed on its own stream with HIP events
-around each launch (the host is made to run ahead of the GPU so that no host gap is
-counted), which gives the roofline figure.  The BF16-cache variant of the same step runs
-alongside for comparison, and the CPU oracle is timed on a bounded sample of the workload.
+timed replays.  The decode_split kernel is also timed on its own: the split launches of all
+layers back to back in a HIP graph, events around the replays, which gives the roofline
+figure.  The roofline's `traffic` (HBM bytes per split launch) comes from a committed counter
+summary (FETCH_SIZE and WRITE_SIZE runs of `--pmc-workload`, scaled by a copy kernel of known
+size) and is reported only while the kernel source matches the one it was measured on.  The
+BF16-cache variant of the same step runs alongside for comparison, and the CPU oracle is timed
+on a bounded sample of the workload.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -48,6 +51,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU seconds for the oracle sample")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    p.add_argument("--pmc-workload", action="store_true",
+                   help="run only the calibration copy and the decode_split launches (under rocprofv3 --pmc)")
+    p.add_argument("--pmc-summarize", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
+                   help="write the HBM-traffic summary from the two counter runs of --pmc-workload")
     return p.parse_args()
 
 
@@ -149,20 +156,149 @@ def sleep_cycles_for(torch, ms):
 
 
 def time_split_kernel(torch, K, layers, mcl, ns, ws, passes):
-    """Average duration (us) of one decode_split launch, HIP events around each launch on the
-    launch stream; a GPU-side spin lets the host enqueue a whole pass ahead of the GPU."""
-    cycles = sleep_cycles_for(torch, 3.0)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
-    durs = []
-    for _ in range(passes):
-        torch.cuda._sleep(cycles)
-        for (a, b), L in zip(pairs, layers):
-            a.record()
+    """Average duration (us) of one decode_split launch: the launches of all layers back to back
+    (the same kernels the step runs, without the write and merge between them), captured once
+    into a HIP graph and replayed; HIP events on the replay stream bracket `passes` replays."""
+    def split_only():
+        for L in layers:
             K.decode_partials(L.cache, L.q, L.bt, L.lens, mcl, ns, ws)
-            b.record()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        split_only()
         torch.cuda.synchronize()
-        durs.extend(a.elapsed_time(b) * 1e3 for a, b in pairs)
-    return float(np.mean(durs)), float(np.median(durs))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            split_only()
+        graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(passes):
+            graph.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (passes * len(layers))
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_i8_long32k_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_kernels.hip")
+
+
+def kernel_source_digest():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode_split launch from the committed counter summary, or None when that
+    summary is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                if line.startswith("{"):
+                    rec = json.loads(line)
+                    if rec.get("kernel_source_sha256") == kernel_source_digest():
+                        return rec
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes
+
+
+def pmc_workload(args):
+    """Runs what the HBM-traffic counters are taken on: a plain copy kernel of known size (the
+    calibration), then the decode_split launches of every layer, a few times each."""
+    import torch
+
+    import decode_attention_quantized_amd as K
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.config]
+    n_layers = args.layers or cfg.layers
+    states, _, lay = prepare(args.config, n_layers, ["int8"], 0)
+    S, Hq = lay.S, cfg.num_q_heads
+    mcl = int(lay.context_lens.max())
+    layers = states["int8"]
+    ns = args.splits or K.choose_num_splits(layers[0].cache, S, Hq, mcl)
+    ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)  # one elementwise kernel: COPY_BYTES read, COPY_BYTES written
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for L in layers:
+            K.decode_partials(L.cache, L.q, L.bt, L.lens, mcl, ns, ws)
+    torch.cuda.synchronize()
+    log(f"pmc workload done: splits {ns}")
+
+
+def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
+    """Turns the two counter runs of pmc_workload into the traffic summary bench.py reads."""
+    import csv
+
+    def per_dispatch(path, counter):
+        split, copy = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
+                if "decode_split_i8_kernel" in r["Kernel_Name"]:
+                    split.append(v)
+                elif "bitwise_not" in r["Kernel_Name"]:
+                    copy.append(v)
+        return float(np.median(split)), float(np.median(copy)), len(split), len(copy)
+
+    fs, fc, nfs, nfc = per_dispatch(fetch_csv, "FETCH_SIZE")
+    ws_, wc, nws, nwc = per_dispatch(write_csv, "WRITE_SIZE")
+    kf, kw = COPY_BYTES / fc, COPY_BYTES / wc
+    import workloads as W
+    cfg = W.CONFIGS[3]
+    layer_bytes = algorithmic_bytes(np.array(cfg.context_lens), cfg.num_kv_heads, cfg.head_dim, "int8")
+    rec = {
+        "kernel": "decode_split_i8_kernel<256,4>",
+        "workload": "long-32k layer: batch 1, context 32768, 24/4 heads, head_dim 256",
+        "kernel_source_sha256": kernel_source_digest(),
+        "fetch_kib_per_launch_raw": round(fs / 1024, 1), "write_kib_per_launch_raw": round(ws_ / 1024, 1),
+        "copy_fetch_kib_raw": round(fc / 1024, 1), "copy_write_kib_raw": round(wc / 1024, 1),
+        "copy_bytes": COPY_BYTES, "fetch_factor": round(kf, 4), "write_factor": round(kw, 4),
+        "fetch_bytes_per_launch": int(fs * kf), "write_bytes_per_launch": int(ws_ * kw),
+        "traffic_bytes_per_launch": int(fs * kf + ws_ * kw), "algorithmic_bytes_per_launch": layer_bytes,
+        "dispatches": {"split_fetch": nfs, "split_write": nws, "copy_fetch": nfc, "copy_write": nwc},
+    }
+    text = [
+        "# HBM traffic: decode_split_i8_kernel<256,4>, long-32k layer (context 32768, 24/4 heads, D 256)",
+        "",
+        "Two counter runs of the same program, one counter each (commands from the repository root",
+        "on one MI355X; `$REPO` is the repository root):",
+        "",
+        "```", cmd_fetch, cmd_write, "```",
+        "",
+        "Per dispatch, medians.  Each counter is scaled by what it reads for a plain copy kernel of",
+        f"{COPY_BYTES} bytes (torch bitwise_not of an int32 tensor: {COPY_BYTES} read, {COPY_BYTES} written).",
+        "",
+        "| | raw KiB | factor | bytes |",
+        "|---|---|---|---|",
+        f"| split FETCH_SIZE | {fs / 1024:.1f} | {kf:.4f} | {int(fs * kf)} |",
+        f"| split WRITE_SIZE | {ws_ / 1024:.1f} | {kw:.4f} | {int(ws_ * kw)} |",
+        f"| copy FETCH_SIZE | {fc / 1024:.1f} | | {COPY_BYTES} |",
+        f"| copy WRITE_SIZE | {wc / 1024:.1f} | | {COPY_BYTES} |",
+        "",
+        f"Algorithmic bytes per launch: {layer_bytes}; measured / algorithmic = "
+        f"{(fs * kf + ws_ * kw) / layer_bytes:.3f}.  The record below is what bench.py reads (it reports",
+        "it only while the kernel source still has the digest it was taken on):",
+        "",
+        json.dumps(rec),
+        "",
+    ]
+    with open(TRAFFIC_SUMMARY, "w") as f:
+        f.write("\n".join(text))
+    print("\n".join(text))
 
 
 def cpu_baseline(host, states_int8, budget_s):
@@ -196,6 +332,9 @@ def cpu_baseline(host, states_int8, budget_s):
 
 def main():
     args = parse()
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this decode-attention path runs on a single MI355X "
               "(see the sharding notes); run it with --gpus 1.", file=sys.stderr)
@@ -205,6 +344,9 @@ def main():
     import decode_attention_quantized_amd as K
     import workloads as W
 
+    if args.pmc_workload:
+        pmc_workload(args)
+        return
     torch.cuda.set_device(0)
     cfg = W.CONFIGS[args.config]
     n_layers = args.layers or cfg.layers
@@ -224,11 +366,11 @@ def main():
         step = make_step(K, layers, S, Hq, mcl, ns, ws)
         ms, wall_ms = time_step(torch, step, args.steps, args.warmup, args.eager)
         step_bytes = algorithmic_bytes(lens, Hkv, D, d) * n_layers
-        kern_mean, kern_med = time_split_kernel(torch, K, layers, mcl, ns, ws, passes=min(args.steps, 20))
-        results[d] = dict(ms=ms, wall_ms=wall_ms, ns=ns, step_bytes=step_bytes, kern_us=kern_mean,
-                          kern_med_us=kern_med, layer_bytes=algorithmic_bytes(lens, Hkv, D, d))
+        kern_us = time_split_kernel(torch, K, layers, mcl, ns, ws, passes=max(args.steps, 20))
+        results[d] = dict(ms=ms, wall_ms=wall_ms, ns=ns, step_bytes=step_bytes, kern_us=kern_us,
+                          layer_bytes=algorithmic_bytes(lens, Hkv, D, d))
         log(f"{d}: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}), {step_bytes / ms / 1e6:.0f} GB/s, "
-            f"decode_split {kern_mean:.2f} us/launch (median {kern_med:.2f}), splits {ns}")
+            f"decode_split {kern_us:.2f} us/launch, splits {ns}")
 
     r = results["int8"]
     value = r["step_bytes"] / (r["ms"] * 1e-3) / 1e9
@@ -267,6 +409,10 @@ def main():
             "avg_launch_us": round(r["kern_us"], 3),
         },
     }
+    tr = measured_traffic() if (args.config == 3 and D == 256) else None
+    if tr is not None:
+        out["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
+        out["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_SUMMARY, ROOT)
     if "bf16" in results:
         b = results["bf16"]
         out["bf16_variant"] = {
