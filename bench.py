@@ -3,7 +3,9 @@
 
 One step = every layer of the workload, each layer being: kv_write of the step's new token
 (quantize-on-write into the paged INT8 cache), decode_split (split-KV GQA attention over the
-cache) and decode_merge (log-sum-exp merge).  Each layer has its own cache, so a step streams
+cache) and decode_merge (log-sum-exp merge).  The timed step uses kvq_decode_step, where the
+split kernel writes the new token itself (two launches per layer); the same work as three
+launches per layer (kvq_write, then the split and merge kernels) is timed beside it.  Each layer has its own cache, so a step streams
 the whole multi-layer cache from HBM (1.06 GiB of INT8 K/V at 32K context, far above the
 256 MB Infinity Cache).  Inputs are seeded synthetic tensors with the workload's shapes and
 value distribution, resident in HBM before the timed region.
@@ -105,13 +107,19 @@ def prepare(cid, n_layers, dtypes, keep_host_layers):
     return states, host, lay
 
 
-def make_step(K, layers, S, Hq, mcl, ns, ws):
-    def step():
+def make_step(K, layers, S, Hq, mcl, ns, ws, fused=True):
+    """One step over every layer.  fused: kvq_decode_step (the new token's write inside the split
+    kernel, then the merge); else three launches per layer: kv_write, decode_split, decode_merge."""
+    def step_fused():
+        for L in layers:
+            K.decode_step(L.cache, L.k_new, L.v_new, L.q, L.bt, L.lens, mcl, ns, out=L.out, lse=L.lse, workspace=ws)
+
+    def step_unfused():
         for L in layers:
             K.write(L.cache, L.k_new, L.v_new, L.slot_new)
             K.decode_partials(L.cache, L.q, L.bt, L.lens, mcl, ns, ws)
             K.decode_merge(L.cache, L.lens, mcl, S, Hq, ns, ws, L.out, L.lse)
-    return step
+    return step_fused if fused else step_unfused
 
 
 def time_step(torch, step, steps, warmup, eager):
@@ -363,14 +371,17 @@ def main():
         layers = states[d]
         ns = args.splits or K.choose_num_splits(layers[0].cache, S, Hq, mcl)
         ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
-        step = make_step(K, layers, S, Hq, mcl, ns, ws)
-        ms, wall_ms = time_step(torch, step, args.steps, args.warmup, args.eager)
+        ms_unfused, _ = time_step(torch, make_step(K, layers, S, Hq, mcl, ns, ws, fused=False), args.steps,
+                                  args.warmup, args.eager)
+        ms, wall_ms = time_step(torch, make_step(K, layers, S, Hq, mcl, ns, ws), args.steps, args.warmup,
+                                args.eager)
         step_bytes = algorithmic_bytes(lens, Hkv, D, d) * n_layers
         kern_us = time_split_kernel(torch, K, layers, mcl, ns, ws, passes=max(args.steps, 20))
-        results[d] = dict(ms=ms, wall_ms=wall_ms, ns=ns, step_bytes=step_bytes, kern_us=kern_us,
-                          layer_bytes=algorithmic_bytes(lens, Hkv, D, d))
-        log(f"{d}: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}), {step_bytes / ms / 1e6:.0f} GB/s, "
-            f"decode_split {kern_us:.2f} us/launch, splits {ns}")
+        results[d] = dict(ms=ms, wall_ms=wall_ms, ms_unfused=ms_unfused, ns=ns, step_bytes=step_bytes,
+                          kern_us=kern_us, layer_bytes=algorithmic_bytes(lens, Hkv, D, d))
+        log(f"{d}: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}; three kernels per layer "
+            f"{ms_unfused * 1e3:.1f}), {step_bytes / ms / 1e6:.0f} GB/s, decode_split {kern_us:.2f} us/launch, "
+            f"splits {ns}")
 
     r = results["int8"]
     value = r["step_bytes"] / (r["ms"] * 1e-3) / 1e9
@@ -384,6 +395,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(r["ms"], 4),
         "us_per_step": round(r["ms"] * 1e3, 1),
+        "us_per_step_unfused": round(r["ms_unfused"] * 1e3, 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 1),
         "higher_is_better": True,
         "scaling": "weak",
@@ -391,7 +403,8 @@ def main():
         "dtype": "int8",
         "data": "synthetic (seeded N(0,1) K/V/Q with x20 outlier channels, bf16; random block-table permutation)",
         "config": {
-            "workload": f"{cfg.name}: {n_layers} layers x (kv_write 1 token/seq + decode_split + decode_merge), "
+            "workload": f"{cfg.name}: {n_layers} layers x (decode_split with the new token's kv_write fused in "
+                        f"+ decode_merge), "
                         f"batch {S}, context {mcl}, {Hq} Q / {Hkv} KV heads, head_dim {D}, INT8 q8_0 16-token pages",
             "layers": n_layers, "batch": S, "context": mcl, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": D, "num_splits": r["ns"], "timing": "eager" if args.eager else "hip-graph replay",
@@ -417,6 +430,7 @@ def main():
         b = results["bf16"]
         out["bf16_variant"] = {
             "us_per_step": round(b["ms"] * 1e3, 1),
+            "us_per_step_unfused": round(b["ms_unfused"] * 1e3, 1),
             "GB_per_s": round(b["step_bytes"] / (b["ms"] * 1e-3) / 1e9, 1),
             "decode_split_us": round(b["kern_us"], 3),
             "int8_speedup_step": round(b["ms"] / r["ms"], 3),

@@ -7,6 +7,7 @@ library itself never allocates.  Importing this package fails if the library is 
     cache = Cache("int8", num_blocks, num_kv_heads, head_dim)          # device planes
     write(cache, k, v, slot_mapping)                                   # quantize-on-write
     out, lse = decode(cache, q, block_tables, context_lens, max_context_len)
+    out, lse = decode_step(cache, k_new, v_new, q, block_tables, context_lens, max_context_len)
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["Cache", "KvqError", "write", "decode", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
+__all__ = ["Cache", "KvqError", "write", "decode", "decode_step", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
            "status_string", "lib", "LIB_PATH", "INT8", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -23,7 +24,7 @@ INT8, BF16 = 0, 1
 PAGE = 16
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m decode_attention_quantized_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python decode_attention_quantized_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 _P = ctypes.c_void_p
@@ -50,6 +51,11 @@ lib.kvq_decode_attention.argtypes = _DEC
 lib.kvq_decode_attention.restype = ctypes.c_int
 lib.kvq_check_decode.argtypes = _DEC
 lib.kvq_check_decode.restype = ctypes.c_int
+_STEP = [_CP, _P, _P] + _DEC[1:]
+lib.kvq_decode_step.argtypes = _STEP
+lib.kvq_decode_step.restype = ctypes.c_int
+lib.kvq_check_decode_step.argtypes = _STEP
+lib.kvq_check_decode_step.restype = ctypes.c_int
 lib.kvq_decode_partials.argtypes = [_CP, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _P, ctypes.c_size_t, _P]
 lib.kvq_decode_partials.restype = ctypes.c_int
 lib.kvq_decode_merge.argtypes = [_CP, _P, _i32, _i32, _i32, _i32, _P, ctypes.c_size_t, _P, _P, _P]
@@ -162,9 +168,7 @@ def page_offset(dtype: int, head_dim: int, which: int, token: int, channel: int)
     return int(lib.kvq_page_offset(dtype, head_dim, which, token, channel))
 
 
-def decode(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int = 0, *,
-           out=None, lse=None, workspace=None, want_lse: bool = True, checked: bool = False, stream=None):
-    """Split-KV decode attention; returns (out fp32 [S][Hq][D], lse fp32 [S][Hq] or None)."""
+def _decode_args(cache, q, block_tables, context_lens, max_context_len, num_splits, out, lse, workspace, want_lse):
     q = _as_bits16(q)
     S, Hq, D = (int(x) for x in q.shape)
     if D != cache.head_dim or not q.is_contiguous():
@@ -182,11 +186,35 @@ def decode(cache: Cache, q, block_tables, context_lens, max_context_len: int, nu
     need = workspace_bytes(cache, S, Hq, ns)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    args = [_ptr(q), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), S, Hq,
+            int(ns), _ptr(out), _ptr(lse), _ptr(workspace), int(workspace.numel() * workspace.element_size())]
+    return args, out, lse
+
+
+def decode(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int = 0, *,
+           out=None, lse=None, workspace=None, want_lse: bool = True, checked: bool = False, stream=None):
+    """Split-KV decode attention; returns (out fp32 [S][Hq][D], lse fp32 [S][Hq] or None)."""
+    args, out, lse = _decode_args(cache, q, block_tables, context_lens, max_context_len, num_splits, out, lse,
+                                  workspace, want_lse)
     fn = lib.kvq_check_decode if checked else lib.kvq_decode_attention
-    st = fn(ctypes.byref(cache.desc), _ptr(q), _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
-            int(max_context_len), S, Hq, int(ns), _ptr(out), _ptr(lse), _ptr(workspace),
-            int(workspace.numel() * workspace.element_size()), _stream(stream))
-    _check(st, "kvq_decode_attention")
+    _check(fn(ctypes.byref(cache.desc), *args, _stream(stream)), "kvq_decode_attention")
+    return out, lse
+
+
+def decode_step(cache: Cache, k_new, v_new, q, block_tables, context_lens, max_context_len: int,
+                num_splits: int = 0, *, out=None, lse=None, workspace=None, want_lse: bool = True,
+                checked: bool = False, stream=None):
+    """One decode step: k_new, v_new [S][Hkv][D] bf16 (token context_lens[s]-1 of each sequence)
+    are written into the cache by the split kernel, then attention and merge as ``decode``."""
+    k_new, v_new = _as_bits16(k_new), _as_bits16(v_new)
+    S = int(q.shape[0])
+    if tuple(k_new.shape) != (S, cache.num_kv_heads, cache.head_dim) or tuple(v_new.shape) != tuple(k_new.shape) \
+            or not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError(f"k_new/v_new must be contiguous [{S}][{cache.num_kv_heads}][{cache.head_dim}] bf16")
+    args, out, lse = _decode_args(cache, q, block_tables, context_lens, max_context_len, num_splits, out, lse,
+                                  workspace, want_lse)
+    fn = lib.kvq_check_decode_step if checked else lib.kvq_decode_step
+    _check(fn(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), *args, _stream(stream)), "kvq_decode_step")
     return out, lse
 
 

@@ -1,6 +1,6 @@
 """Build libkvq.so in-tree with hipcc for gfx950.
 
-    python -m decode_attention_quantized_amd.build
+    python decode_attention_quantized_amd/build.py
 
 The HIP sources are compiled with packed-FP32 instructions disabled and with IEEE fp32
 division/rounding (no fast-math): the quantizer must match a correctly rounded reference

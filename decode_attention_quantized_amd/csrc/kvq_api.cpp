@@ -128,6 +128,8 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   a.ml = reinterpret_cast<float2 *>(static_cast<char *>(const_cast<void *>(workspace)) + o_bytes);
   a.out = out;
   a.lse = lse;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.S = num_seqs;
@@ -142,14 +144,19 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   return KVQ_OK;
 }
 
-int decode_impl(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
-                const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
-                int32_t num_splits, float *out, float *lse, void *workspace, size_t workspace_bytes_given,
-                void *stream) {
+// k_new / v_new: the step's new tokens (fused quantize-on-write), or null for attention only.
+int decode_impl(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out,
+                float *lse, void *workspace, size_t workspace_bytes_given, void *stream) {
   kvq::DecodeArgs a;
   int st = prepare_decode(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                           num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, true, true, a);
   if (st != KVQ_OK) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return KVQ_ERR_INVALID_ARG;
+  if (k_new && (!aligned(k_new, 16) || !aligned(v_new, 16))) return KVQ_ERR_INVALID_ARG;
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kvq::launch_decode_split(cache->dtype, a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
   if (kvq::launch_decode_merge(a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
@@ -190,6 +197,65 @@ bool to_host(std::vector<T> &dst, const void *src, size_t n, hipStream_t st) {
   return hipStreamSynchronize(st) == hipSuccess;
 }
 
+bool all_finite(const std::vector<uint16_t> &x) {
+  for (uint16_t b : x)
+    if (!bf16_finite(b)) return false;
+  return true;
+}
+
+// Checked mode of decode (and of the fused step when k_new != null): host copies of the metadata
+// and inputs, validated against the contract, then the fast path and a synchronisation.
+int check_decode_impl(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out,
+                      float *lse, void *workspace, size_t workspace_bytes_given, void *stream) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = check_heads(cache, num_q_heads);
+  if (st != KVQ_OK) return st;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || !q || !block_tables || !context_lens) return KVQ_ERR_INVALID_ARG;
+  if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage)
+    return KVQ_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (is_capturing(s)) return KVQ_ERR_CAPTURING;
+  std::vector<int32_t> lens, tables;
+  if (!to_host(lens, context_lens, (size_t)num_seqs, s)) return KVQ_ERR_LAUNCH_FAILED;
+  if (!to_host(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq, s)) return KVQ_ERR_LAUNCH_FAILED;
+  std::unordered_set<int32_t> new_blocks;
+  for (int i = 0; i < num_seqs; ++i) {
+    const int32_t L = lens[i];
+    if (L < 0 || L > max_context_len) return KVQ_ERR_VALIDATION_FAILED;
+    const int pages = (L + kvq::kPage - 1) / kvq::kPage;
+    for (int p = 0; p < pages; ++p) {
+      const int32_t b = tables[(size_t)i * max_blocks_per_seq + p];
+      if (b < 0 || b >= cache->num_blocks) return KVQ_ERR_VALIDATION_FAILED;
+    }
+    if (k_new && pages > 0 && !new_blocks.insert(tables[(size_t)i * max_blocks_per_seq + pages - 1]).second)
+      return KVQ_ERR_VALIDATION_FAILED;  // two sequences write into one block
+  }
+  if (k_new) {  // no other sequence may read a block that receives a new token
+    for (int i = 0; i < num_seqs; ++i) {
+      const int pages = (lens[i] + kvq::kPage - 1) / kvq::kPage;
+      for (int p = 0; p + 1 < pages; ++p)
+        if (new_blocks.count(tables[(size_t)i * max_blocks_per_seq + p])) return KVQ_ERR_VALIDATION_FAILED;
+    }
+  }
+  std::vector<uint16_t> hq;
+  if (!to_host(hq, q, (size_t)num_seqs * num_q_heads * cache->head_dim, s)) return KVQ_ERR_LAUNCH_FAILED;
+  if (!all_finite(hq)) return KVQ_ERR_VALIDATION_FAILED;
+  if (k_new) {
+    if (!v_new) return KVQ_ERR_INVALID_ARG;
+    std::vector<uint16_t> hk, hv;
+    const size_t n = (size_t)num_seqs * cache->num_kv_heads * cache->head_dim;
+    if (!to_host(hk, k_new, n, s) || !to_host(hv, v_new, n, s)) return KVQ_ERR_LAUNCH_FAILED;
+    if (!all_finite(hk) || !all_finite(hv)) return KVQ_ERR_VALIDATION_FAILED;
+  }
+  st = decode_impl(cache, k_new, v_new, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                   num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+  if (st != KVQ_OK) return st;
+  return hipStreamSynchronize(s) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH_FAILED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -220,8 +286,26 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
                          void *workspace, size_t workspace_bytes_given, void *stream) {
-  return decode_impl(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
-                     num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+  return decode_impl(cache, nullptr, nullptr, q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                     num_seqs, num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+}
+
+int kvq_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out,
+                    float *lse, void *workspace, size_t workspace_bytes_given, void *stream) {
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  return decode_impl(cache, k_new, v_new, q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                     num_seqs, num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+}
+
+int kvq_check_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                          const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                          float *out, float *lse, void *workspace, size_t workspace_bytes_given, void *stream) {
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  return check_decode_impl(cache, k_new, v_new, q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                           num_seqs, num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
 }
 
 int kvq_decode_partials(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
@@ -280,35 +364,9 @@ int kvq_check_decode(const kvq_cache_t *cache, const void *q, const int32_t *blo
                      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
                      int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
                      void *workspace, size_t workspace_bytes_given, void *stream) {
-  int st = check_cache(cache);
-  if (st != KVQ_OK) return st;
-  st = check_heads(cache, num_q_heads);
-  if (st != KVQ_OK) return st;
-  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || !q || !block_tables || !context_lens) return KVQ_ERR_INVALID_ARG;
-  if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage)
-    return KVQ_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (is_capturing(s)) return KVQ_ERR_CAPTURING;
-  std::vector<int32_t> lens, tables;
-  if (!to_host(lens, context_lens, (size_t)num_seqs, s)) return KVQ_ERR_LAUNCH_FAILED;
-  if (!to_host(tables, block_tables, (size_t)num_seqs * max_blocks_per_seq, s)) return KVQ_ERR_LAUNCH_FAILED;
-  for (int i = 0; i < num_seqs; ++i) {
-    const int32_t L = lens[i];
-    if (L < 0 || L > max_context_len) return KVQ_ERR_VALIDATION_FAILED;
-    const int pages = (L + kvq::kPage - 1) / kvq::kPage;
-    for (int p = 0; p < pages; ++p) {
-      const int32_t b = tables[(size_t)i * max_blocks_per_seq + p];
-      if (b < 0 || b >= cache->num_blocks) return KVQ_ERR_VALIDATION_FAILED;
-    }
-  }
-  std::vector<uint16_t> hq;
-  if (!to_host(hq, q, (size_t)num_seqs * num_q_heads * cache->head_dim, s)) return KVQ_ERR_LAUNCH_FAILED;
-  for (uint16_t b : hq)
-    if (!bf16_finite(b)) return KVQ_ERR_VALIDATION_FAILED;
-  st = decode_impl(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_q_heads,
-                   num_splits, out, lse, workspace, workspace_bytes_given, stream);
-  if (st != KVQ_OK) return st;
-  return hipStreamSynchronize(s) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH_FAILED;
+  return check_decode_impl(cache, nullptr, nullptr, q, block_tables, max_blocks_per_seq, context_lens,
+                           max_context_len, num_seqs, num_q_heads, num_splits, out, lse, workspace,
+                           workspace_bytes_given, stream);
 }
 
 int32_t kvq_page_offset(int32_t dtype, int32_t head_dim, int32_t which, int32_t token, int32_t channel) {

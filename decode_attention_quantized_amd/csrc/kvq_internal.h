@@ -24,6 +24,8 @@ struct DecodeArgs {
   float2 *ml;                     // workspace: (max in log2 units, sum) [S][Hq][NS]
   float *out;                     // fp32 [S][Hq][D]
   float *lse;                     // fp32 [S][Hq] or null
+  const uint16_t *k_new, *v_new;  // bf16 [S][Hkv][D]: token context_len-1 of each sequence, quantized
+                                  // into its page by the split kernel before the page is read (or null)
   int max_blocks, max_context_len, S, Hq, Hkv, G, NB, NS, cpp, D;
   int waves;                      // wavefronts per split workgroup (1, 2, 4 or 8)
 };

@@ -115,6 +115,19 @@ __device__ __forceinline__ float scale_at(const u4_t (&w)[N], int e) {
 
 // ------------------------------------------------------------------ quantize-on-write
 
+// The fp16 scale of a group with maximum magnitude amax: fp16(min(amax / 127, 65504)), an fp32
+// division and a round to nearest even.
+__device__ __forceinline__ _Float16 q8_scale(float amax) { return (_Float16)fminf(amax / 127.0f, 65504.0f); }
+
+// The code of x against the stored scale s (as fp32): rint(x / s) (nearest even) clamped to
+// +-127; 0 when s is 0 or x / s is NaN.  Returned as the code's byte.
+__device__ __forceinline__ uint32_t q8_code(float x, float s) {
+  float q = __builtin_rintf(x / s);
+  q = (q != q) ? 0.0f : fminf(fmaxf(q, -127.0f), 127.0f);
+  q = (s != 0.0f) ? q : 0.0f;
+  return (uint32_t)(int)q & 0xFFu;
+}
+
 // One thread per (token, KV head, K or V, 32-channel group).
 template <int D>
 __global__ __launch_bounds__(256) void kv_write_i8_kernel(WriteArgs a) {
@@ -146,22 +159,13 @@ __global__ __launch_bounds__(256) void kv_write_i8_kernel(WriteArgs a) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  const float d = fminf(amax / 127.0f, 65504.0f);
-  const _Float16 s16 = (_Float16)d;
+  const _Float16 s16 = q8_scale(amax);
   const float s = (float)s16;
   uint32_t packed[kGroup / 4];
 #pragma unroll
   for (int i = 0; i < kGroup / 4; ++i) packed[i] = 0u;
 #pragma unroll
-  for (int i = 0; i < kGroup; ++i) {
-    float q = 0.0f;
-    if (s != 0.0f) {
-      q = __builtin_rintf(x[i] / s);
-      if (q != q) q = 0.0f;
-      q = fminf(fmaxf(q, -127.0f), 127.0f);
-    }
-    packed[i >> 2] |= ((uint32_t)(int)q & 0xFFu) << (8 * (i & 3));
-  }
+  for (int i = 0; i < kGroup; ++i) packed[i >> 2] |= q8_code(x[i], s) << (8 * (i & 3));
   const int64_t page = (int64_t)blk * a.Hkv + h;
   const uint16_t sbits = __builtin_bit_cast(uint16_t, s16);
   if (which == 0) {
@@ -281,6 +285,91 @@ __device__ __forceinline__ void load_q(const DecodeArgs &a, int s, int h, int n1
   for (int g = 0; g < D / 32; ++g) qraw[g] = ld16(r, off, g * kGroup * 2);
 }
 
+// ---- quantize-on-write of the step's new token, fused into the split kernel
+//
+// In a decode step the token at position L - 1 of each sequence is new.  The wavefront that owns
+// the sequence's last page (for its KV head) writes the token into that page before it requests
+// the page; its own later loads of those bytes follow its stores in order.  Lane l handles
+// channels 4l .. 4l + 3 of the K and V rows; lanes with 4l >= D hold zeros and store nothing.
+
+// Requests the new token's K and V rows (4 bf16 per lane); zeros unless `own`.
+template <int D>
+__device__ __forceinline__ void load_new_rows(const DecodeArgs &a, int s, int h, bool own, int lane, u2_t &kr,
+                                              u2_t &vr) {
+  const int64_t row = ((int64_t)s * a.Hkv + h) * D;
+  const int bytes = own ? 2 * D : 0;
+  const uint16_t *kb = own ? a.k_new + row : a.q, *vb = own ? a.v_new + row : a.q;
+  kr = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(kb), 0, bytes, 0x00020000),
+                                    lane * 8, 0, 0));
+  vr = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(
+                                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(vb), 0, bytes, 0x00020000),
+                                    lane * 8, 0, 0));
+}
+
+// Passes the rows through an empty asm at the top of the write, so that no part of the write
+// (which waits for the rows) is hoisted above the branch that selects the writing wave.
+__device__ __forceinline__ void pin_rows(u2_t &kr, u2_t &vr) {
+  uint32_t k0 = kr[0], k1 = kr[1], v0 = vr[0], v1 = vr[1];
+  asm("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
+  kr = u2_t{k0, k1};
+  vr = u2_t{v0, v1};
+}
+
+// INT8 cache: the group maximum is reduced over the 8 lanes of each 32-channel group; scale and
+// codes follow the same arithmetic as kv_write (q8_scale, q8_code), so the bytes are identical.
+template <int D>
+__device__ __forceinline__ void write_new_i8(const DecodeArgs &a, int64_t page, int t, u2_t kr, u2_t vr, int lane) {
+  constexpr int NG = D / kGroup;
+  pin_rows(kr, vr);
+  const int c0 = 4 * lane;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint32_t w0 = which ? vr[0] : kr[0], w1 = which ? vr[1] : kr[1];
+    const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    const _Float16 s16 = q8_scale(amax);
+    const float sc = (float)s16;
+    uint32_t codes = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) codes |= q8_code(x[i], sc) << (8 * i);
+    if (c0 < D) {
+      int8_t *dst = static_cast<int8_t *>(const_cast<void *>(which ? a.vc : a.kc)) + page * (kPage * D);
+      if (which == 0) {
+        *reinterpret_cast<uint32_t *>(dst + i8_k_offset(t, c0)) = codes;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i8_v_offset(t, c0 + i)] = (int8_t)((codes >> (8 * i)) & 0xFFu);
+      }
+      if ((lane & 7) == 0)
+        const_cast<uint16_t *>(which ? a.vs : a.ks)[(page * NG + (c0 >> 5)) * kPage + t] =
+            __builtin_bit_cast(uint16_t, s16);
+    }
+  }
+}
+
+// BF16 cache: a copy of the two rows into the page.
+template <int D>
+__device__ __forceinline__ void write_new_bf16(const DecodeArgs &a, int64_t page, int t, u2_t kr, u2_t vr, int lane) {
+  pin_rows(kr, vr);
+  const int c0 = 4 * lane;
+  if (c0 < D) {
+    uint16_t *kd = static_cast<uint16_t *>(const_cast<void *>(a.kc)) + page * (kPage * D);
+    uint16_t *vd = static_cast<uint16_t *>(const_cast<void *>(a.vc)) + page * (kPage * D);
+    *reinterpret_cast<u2_t *>(kd + bf16_k_offset(t, c0)) = kr;
+    const uint32_t v01 = vr[0], v23 = vr[1];
+    vd[bf16_v_offset(t, c0)] = (uint16_t)(v01 & 0xFFFFu);
+    vd[bf16_v_offset(t, c0 + 1)] = (uint16_t)(v01 >> 16);
+    vd[bf16_v_offset(t, c0 + 2)] = (uint16_t)(v23 & 0xFFFFu);
+    vd[bf16_v_offset(t, c0 + 3)] = (uint16_t)(v23 >> 16);
+  }
+}
+
 // Merge scratch of one wave (floats): its accumulator tiles as [tile][lane][4], then m[16]
 // and l[16].
 template <int D>
@@ -369,7 +458,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
 // requested before anything else.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_i8_kernel(DecodeArgs a) {
+void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
   constexpr int NG = D / kGroup;      // scale groups
   constexpr int NT = D / 16;          // output tiles
   constexpr int NL = D / 64;          // 16-byte code loads per lane per page
@@ -381,7 +470,6 @@ void decode_split_i8_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];              // rescale factors, per head
   extern __shared__ float s_merge[];                                          // [NW][G*D + 32] (dynamic)
 
-  const int32_t *__restrict__ block_tables = a.block_tables;
   const int32_t *__restrict__ context_lens = a.context_lens;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
@@ -429,9 +517,19 @@ void decode_split_i8_kernel(DecodeArgs a) {
   int blk[NBUF];
 #pragma unroll
   for (int b = 0; b < NBUF; ++b) blk[b] = block_of(b);
+  // The wave that holds the sequence's last page writes the step's new token into it first (its
+  // local page index k_last; written before that page is requested).
+  const int blk_last = btrow[P - 1];
+  const bool own_new = a.k_new != nullptr && p1 == P && wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
+  const int k_last = (n_units - 1) / NW;
   u4_t qraw[NG];
   load_q<D>(a, s, h, n16, q4, qraw);
+  u2_t knew, vnew;
+  load_new_rows<D>(a, s, h, own_new, lane, knew, vnew);
   __builtin_amdgcn_sched_barrier(0);
+  const int64_t page_new = (int64_t)blk_last * a.Hkv + h;
+  const int t_new = (L - 1) & (kPage - 1);
+  if (own_new && k_last == 0) write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
   issue_k(0, 0, blk[0]);
   __builtin_amdgcn_sched_barrier(0);
 
@@ -469,6 +567,7 @@ void decode_split_i8_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
   const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
+  if (own_new && k_last != 0) write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
   // (scheduling barriers keep the loads in this order: the compiler's wait counts follow it)
   issue_v(0, 0, blk[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -623,12 +722,11 @@ __device__ __forceinline__ f4_t mfma16_bf16(s4_t a, s4_t b, f4_t c) {
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_bf16_kernel(DecodeArgs a) {
+void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
   constexpr int NG = D / 32;  // 16-byte loads per lane per page (8 bf16 each)
   constexpr int NT = D / 16;
   constexpr int PAGE_B = kPage * D * 2;
   __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];
-  const int32_t *__restrict__ block_tables = a.block_tables;
   const int32_t *__restrict__ context_lens = a.context_lens;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -646,6 +744,16 @@ void decode_split_bf16_kernel(DecodeArgs a) {
 
   u4_t qraw[NG];
   load_q<D>(a, s, h, n16, q4, qraw);
+  // The wave that holds the sequence's last page writes the step's new token into it before it
+  // requests that page (unit k_last of the wave).
+  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
+  const int blk_last = btrow[P - 1];
+  const bool own_new = a.k_new != nullptr && p1 == P && wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
+  const int k_last = (n_units - 1) / NW;
+  u2_t knew, vnew;
+  load_new_rows<D>(a, s, h, own_new, lane, knew, vnew);
+  const int64_t page_new = (int64_t)blk_last * a.Hkv + h;
+  const int t_new = (L - 1) & (kPage - 1);
   b8_t qop[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) qop[g] = __builtin_bit_cast(b8_t, qraw[g]);
@@ -656,7 +764,6 @@ void decode_split_bf16_kernel(DecodeArgs a) {
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
   const int voff = lane * 16;
   auto page_index = [&](int p) -> int64_t {
     const int b = min(max(btrow[p], 0), a.NB - 1);
@@ -669,12 +776,14 @@ void decode_split_bf16_kernel(DecodeArgs a) {
     for (int i = 0; i < NG; ++i) dst[i] = ld16(r, voff, 1024 * i);
   };
   int u = wave;
+  if (own_new && k_last == 0) write_new_bf16<D>(a, page_new, t_new, knew, vnew, lane);
   {
     const bool ok = u < n_units;
     const int64_t pg = page_index(ok ? p0 + u : p0);
     load(kb, a.kc, pg, ok);
     load(vb, a.vc, pg, ok);
   }
+  if (own_new && k_last != 0) write_new_bf16<D>(a, page_new, t_new, knew, vnew, lane);
   for (; u < n_units; u += NW) {
     const int lim = min(L - (p0 + u) * kPage, kPage);
     const int un = u + NW;
@@ -831,9 +940,9 @@ static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
   const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
   else
-    hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a);
+    hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
 }
 
 template <int D, bool I8>

@@ -21,9 +21,15 @@
  *                        section "Read the compressed cache without copying it first": one
  *                        query token reads the int8 cache directly, V dequantized in registers,
  *                        no converted copy of the cache.
+ *   kvq_decode_step      one decode step of one layer in a single kernel pass: the new token's
+ *                        quantize-on-write (as kvq_write) fused into the split kernel, then the
+ *                        merge (as kvq_decode_attention).  Gllm page, section "Interpretation":
+ *                        at decode batch sizes the extra quantize launches per layer cost more
+ *                        than the quantization saves; section "Known Limitations": graph capture
+ *                        breaks when a kernel of the step allocates (the step allocates nothing).
  *   kvq_check_write,     checked wrappers.  NVFP4 page, section "Testing the cache without
- *   kvq_check_decode     loading the model": a checked API that validates on the host,
- *                        synchronises, and refuses graph capture; raw callers own stream
+ *   kvq_check_decode,    loading the model": a checked API that validates on the host,
+ *   kvq_check_decode_step synchronises, and refuses graph capture; raw callers own stream
  *                        ordering and cache lifetime.
  *
  * Arithmetic.  kvq_write: x = float(bf16); amax = max |x| over 32 consecutive channels of one
@@ -150,6 +156,27 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * One decode step: writes the new token of every sequence into the cache, then attention and
+ * merge over the context that includes it.  The result equals kvq_write(k_new, v_new,
+ * slot_mapping) followed by kvq_decode_attention(...) on the same stream, with slot_mapping[s]
+ * the slot of token context_lens[s]-1 (block_tables[s][(L-1)/16]*16 + (L-1)%16); cache bytes,
+ * out and lse are the same.  The workgroup that reads a sequence's last page (for one KV head)
+ * writes the token into it before reading it, so no separate write kernel runs.
+ *   k_new, v_new   device, bfloat16 [num_seqs][Hkv][D], contiguous, 16-byte aligned: the token
+ *                  at position context_lens[s]-1 of each sequence.
+ *   other arguments as kvq_decode_attention (same workspace size).
+ * A sequence with context_lens[s] == 0 writes nothing; nothing is written when the block of the
+ * last page is outside [0, num_blocks).  Contract (checked by kvq_check_decode_step): the block
+ * that receives a sequence's new token is not used by any other sequence of the call, and not
+ * twice in that sequence's table (blocks shared between sequences hold only older tokens).
+ * Asynchronous on `stream`; allocates nothing.
+ */
+int kvq_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                    int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                    float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The two halves of kvq_decode_attention, for callers that combine partials themselves
  * (for instance partials of one sequence computed in several places) or time the split
  * kernel alone.  kvq_decode_partials writes, for every split that holds pages, the
@@ -173,8 +200,10 @@ int kvq_decode_merge(const kvq_cache_t *cache, const int32_t *context_lens, int3
  * KVQ_ERR_VALIDATION_FAILED before launching, then runs the fast path and synchronises
  * again.  kvq_check_write rejects duplicate valid slots, slots >= num_blocks*16 and
  * non-finite K/V.  kvq_check_decode rejects context_lens outside [0, max_context_len],
- * block ids outside [0, num_blocks) in the pages a sequence uses, and non-finite Q.  Both
- * refuse to run while `stream` is being captured (KVQ_ERR_CAPTURING).
+ * block ids outside [0, num_blocks) in the pages a sequence uses, and non-finite Q;
+ * kvq_check_decode_step also non-finite new K/V and a block that receives a new token while
+ * another sequence (or another page of the same one) uses it.  All refuse to run while `stream`
+ * is being captured (KVQ_ERR_CAPTURING).
  */
 int kvq_check_write(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping,
                     int32_t num_tokens, void *stream);
@@ -182,6 +211,10 @@ int kvq_check_decode(const kvq_cache_t *cache, const void *q, const int32_t *blo
                      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
                      int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
                      void *workspace, size_t workspace_bytes, void *stream);
+int kvq_check_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                          const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                          float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /* In-page offset (bytes for INT8, elements for BF16) of (token 0..15, channel c) in a K
  * (which = 0) or V (which = 1) page, per the layout above; -1 on invalid arguments. */

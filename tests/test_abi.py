@@ -115,6 +115,27 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(d, wsb=need - 1) == -3
 
 
+def _step(desc, kn=FAKE, vn=FAKE, q=FAKE, bt=FAKE, mb=32, cl=FAKE, mcl=512, S=1, Hq=24, ns=4, out=FAKE, lse=None,
+          ws=FAKE, wsb=1 << 30):
+    return K.lib.kvq_decode_step(ctypes.byref(desc), kn, vn, q, bt, mb, cl, mcl, S, Hq, ns, out, lse, ws, wsb, None)
+
+
+def test_decode_step_rejects_invalid_arguments():
+    d = _desc()
+    assert _step(d, kn=None) == -1                     # the new token is required
+    assert _step(d, vn=None) == -1
+    assert _step(d, kn=FAKE + 8) == -1                 # not 16-aligned
+    assert _step(d, vn=FAKE + 2) == -1
+    assert _step(d, Hq=25) == -1                       # the decode checks apply too
+    assert _step(d, mcl=0) == -1
+    assert _step(d, out=None) == -1
+    assert _step(_desc(d=96)) == -2
+    need = K.lib.kvq_decode_workspace_bytes(ctypes.byref(d), 1, 24, 4)
+    assert _step(d, wsb=need - 1) == -3
+    assert K.lib.kvq_check_decode_step(ctypes.byref(d), None, FAKE, FAKE, FAKE, 32, FAKE, 512, 1, 24, 4, FAKE,
+                                       None, FAKE, 1 << 30, None) == -1
+
+
 def test_workspace_bytes_formula():
     d = _desc()
     for S, Hq, ns, D in [(1, 24, 64, 256), (32, 32, 7, 128), (4, 24, 256, 256)]:

@@ -1,6 +1,7 @@
 """GPU parity at the full sizes of the long-context, mixed-batch and dense-8B workloads (one
-layer each), in the launch configuration the benchmark times: whole-cache byte comparison,
-and every output row against the oracle for each swept split count and the automatic one."""
+layer each), in the launch configuration the benchmark times (the fused step, automatic split
+count): whole-cache byte comparison, and every output row against the oracle, then for each
+swept split count."""
 import numpy as np
 import pytest
 import torch
@@ -20,12 +21,19 @@ def test_fullsize_int8(cid):
     cfg = layer.cfg
     pair = Pair("int8", layer.num_blocks, cfg.num_kv_heads, cfg.head_dim)
     log(f"config {cid}: writing {int(layer.context_lens.sum())} tokens")
-    fill_from_layer(pair, layer)
-    pair.assert_cache_equal()
+    pre, stp = layer.prefill_rows(), layer.step_rows()
+    pair.write(layer.k[pre], layer.v[pre], layer.slots[pre])
+    O.kv_write(pair.o, layer.k[stp], layer.v[stp], layer.slots[stp])
     mcl = int(layer.context_lens.max())
     log(f"config {cid}: oracle decode")
     ref = O.decode(pair.o, layer.q, layer.block_tables, layer.context_lens)
     qd, btd, ld = bf16_dev(layer.q), dev(layer.block_tables), dev(layer.context_lens)
+    # the benchmarked step: the new tokens written by the split kernel, automatic split count
+    log(f"config {cid}: fused decode step")
+    out, lse = K.decode_step(pair.g, bf16_dev(layer.k[stp]), bf16_dev(layer.v[stp]), qd, btd, ld, mcl, 0)
+    torch.cuda.synchronize()
+    pair.assert_cache_equal()
+    assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref[0], ref[1], f"config {cid} fused step")
     for ns in list(cfg.splits) + [0]:
         log(f"config {cid}: decode splits={ns}")
         out, lse = K.decode(pair.g, qd, btd, ld, mcl, ns)
