@@ -408,45 +408,54 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
       mine[NT * 256 + 16 + n16] = l_run;
     }
     __syncthreads();
-    if (4 * q4 < G) {
-      // weights of every wave for this lane's rows (heads 4 q4 .. 4 q4 + 3)
-      f4_t mw[NW], wt[NW];
-      f4_t M = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    // Every lane computes; lanes of padding heads (4 q4 + i >= G) read unused LDS and their stores
+    // fall past the end of the resources below (rows of heads 0 .. G-1 only), so no branches.
+    // weights of every wave for this lane's rows (heads 4 q4 .. 4 q4 + 3)
+    f4_t mw[NW], wt[NW];
+    f4_t M = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        mw[w] = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 4 * q4);
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 4 * q4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], mw[w][i]);
-      }
-      f4_t Lsum = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], mw[w][i]);
+    }
+    f4_t Lsum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const f4_t lw = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 16 + 4 * q4);
+    for (int w = 0; w < NW; ++w) {
+      const f4_t lw = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 16 + 4 * q4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wt[w][i] = (mw[w][i] == -INFINITY) ? 0.0f : exp2_w(mw[w][i] - M[i]);  // waves without pages: 0
-          Lsum[i] = fmaf(wt[w][i], lw[i], Lsum[i]);
-        }
-      }
-      if (wave == 0 && n16 == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * q4 + i < G) a.ml[row0 + (int64_t)(4 * q4 + i) * a.NS] = make_float2(M[i], Lsum[i]);
-      }
-#pragma unroll
-      for (int jt = wave; jt < NT; jt += NW) {
-        f4_t o = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const f4_t v = *reinterpret_cast<const f4_t *>(merge + w * ST + (jt * 64 + lane) * 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = fmaf(wt[w][i], v[i], o[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * q4 + i < G) a.o_part[(row0 + (int64_t)(4 * q4 + i) * a.NS) * D + 16 * jt + n16] = o[i];
+      for (int i = 0; i < 4; ++i) {
+        wt[w][i] = (mw[w][i] == -INFINITY) ? 0.0f : exp2_w(mw[w][i] - M[i]);  // waves without pages: 0
+        Lsum[i] = fmaf(wt[w][i], lw[i], Lsum[i]);
       }
     }
+    const int rows_valid = (G - 1) * a.NS + 1;  // rows from head 0 through head G - 1 of this split
+    if (wave == 0 && n16 == 0) {
+      const auto rml = __builtin_amdgcn_make_buffer_rsrc(a.ml + row0, 0, rows_valid * 8, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u2_t, make_float2(M[i], Lsum[i])), rml, (4 * q4 + i) * a.NS * 8, 0, 0);
+    }
+    const auto ro = __builtin_amdgcn_make_buffer_rsrc(a.o_part + row0 * D, 0, rows_valid * D * 4, 0x00020000);
+    f4_t o[NT / NW];
+#pragma unroll
+    for (int t = 0; t < NT / NW; ++t) {  // every LDS read is issued before the first store
+      const int jt = wave + t * NW;
+      o[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const f4_t v = *reinterpret_cast<const f4_t *>(merge + w * ST + (jt * 64 + lane) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] = fmaf(wt[w][i], v[i], o[t][i]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT / NW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[t][i]), ro,
+                                              ((4 * q4 + i) * a.NS * D + 16 * (wave + t * NW) + n16) * 4, 0, 0);
   }
 }
 
@@ -855,7 +864,7 @@ constexpr int kMergeWaves = 4;
 template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int NCH = D / 64;
-  constexpr int UNR = 8;  // partials requested together per wave
+  constexpr int UNR = 16;  // partials requested together per wave (one round trip up to 64 splits)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int chunk = blockIdx.x % NCH;
