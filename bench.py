@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU seconds for the oracle sample")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    p.add_argument("--sweep", action="store_true",
+                   help="time the step at each of the workload's split counts and the automatic one")
+    p.add_argument("--sweep-out", default="", help="also write the sweep table (markdown) to this path")
     p.add_argument("--pmc-workload", action="store_true",
                    help="run only the calibration copy and the decode_split launches (under rocprofv3 --pmc)")
     p.add_argument("--pmc-summarize", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
@@ -338,6 +341,79 @@ def cpu_baseline(host, states_int8, budget_s):
     return elapsed, nbytes, layers_done, max_err, within
 
 
+FLUSH_BYTES = 512 << 20  # written between steps when the whole cache fits in the 256 MB MALL
+
+
+def sweep(args):
+    """Per dtype and split count: us per step (graph replay of the fused step, one replay per
+    timing, the MALL flushed between replays when the workload's caches would fit in it)."""
+    import torch
+
+    import decode_attention_quantized_amd as K
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.config]
+    n_layers = args.layers or cfg.layers
+    dtypes = ["int8"] if args.no_bf16 else ["int8", "bf16"]
+    states, _, lay = prepare(args.config, n_layers, dtypes, 0)
+    S, Hq, Hkv, D = lay.S, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    mcl = int(lay.context_lens.max())
+    flush = None
+    if algorithmic_bytes(lay.context_lens, Hkv, D, "bf16") * n_layers < 2 * FLUSH_BYTES:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    rows = []
+    for d in dtypes:
+        layers = states[d]
+        auto = K.choose_num_splits(layers[0].cache, S, Hq, mcl)
+        counts = sorted(set(list(cfg.splits) + [auto]))
+        step_bytes = algorithmic_bytes(lay.context_lens, Hkv, D, d) * n_layers
+        for ns in counts:
+            ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
+            step = make_step(K, layers, S, Hq, mcl, ns, ws)
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                step()
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=s):
+                    step()
+                times = []
+                for i in range(args.warmup + args.steps):
+                    if flush is not None:
+                        flush.fill_(i)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(s)
+                    graph.replay()
+                    e1.record(s)
+                    if i >= args.warmup:
+                        times.append((e0, e1))
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in times])) * 1e3
+            rows.append((d, ns, ns == auto, us, step_bytes / (us * 1e-6) / 1e9))
+            log(f"{d} splits {ns}{' (auto)' if ns == auto else ''}: {us:.1f} us/step, {rows[-1][4]:.0f} GB/s")
+            del graph, ws
+    text = [f"# Split-count sweep: {cfg.name} ({n_layers} layers, batch {S}, context "
+            f"{'/'.join(str(int(x)) for x in np.unique(lay.context_lens)) if S <= 8 else f'{int(lay.context_lens.min())}..{mcl}'}, "
+            f"{Hq}/{Hkv} heads, D {D})", "",
+            "Command (run from the repository root on one MI355X):", "", "```",
+            f"python3 bench.py --sweep --config {args.config} --steps {args.steps} --warmup {args.warmup}"
+            + (" --no-bf16" if args.no_bf16 else "") + (f" --sweep-out {args.sweep_out}" if args.sweep_out else ""),
+            "```", "",
+            "Median over the timed steps of one graph replay of the fused step (every layer: decode_split with "
+            "the new token's write, then decode_merge), HIP events on the replay stream."
+            + (f"  A {FLUSH_BYTES >> 20} MiB fill between replays evicts the caches from the 256 MB MALL "
+               "(outside the timed region)." if flush is not None else ""), "",
+            "| cache | splits | auto | us per step | GB/s (algorithmic) |", "|---|---|---|---|---|"]
+    for d, ns, a, us, gbs in rows:
+        text.append(f"| {d} | {ns} | {'yes' if a else ''} | {us:.1f} | {gbs:.0f} |")
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write("\n".join(text) + "\n")
+    print("\n".join(text), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summarize:
@@ -354,6 +430,9 @@ def main():
 
     if args.pmc_workload:
         pmc_workload(args)
+        return
+    if args.sweep:
+        sweep(args)
         return
     torch.cuda.set_device(0)
     cfg = W.CONFIGS[args.config]

@@ -53,15 +53,19 @@ int device_cus() {
 }
 
 // Split count: enough workgroups to fill every compute unit, but no split shorter than a
-// minimum number of pages, so that the merge stays small next to the stream.  The INT8 split
-// kernel runs best with one workgroup (one wave per SIMD) per compute unit and a long page
-// run per wave; the BF16 one with two workgroups per compute unit.
+// minimum number of pages, so that the merge stays small next to the stream.  A single sequence
+// runs best with one workgroup (one wave per SIMD) per compute unit and long page runs per wave.
+// A batch gets two workgroups per compute unit: its sequences' lengths differ, and the second
+// workgroup per CU evens out the longest ones (the host sees only the maximum length).  Both
+// choices come from split-count sweeps of the INT8 and BF16 kernels on 256 CUs (one sequence at
+// 4K and 32K tokens, 4 sequences of 2K-32K, 32 sequences of 512-8K).
 int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus) {
+  (void)dtype;
   (void)D;
   const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
   if (max_pages <= 0) return 1;
   const int64_t base = (int64_t)S * Hkv;
-  const int64_t target_wg = (dtype == KVQ_INT8_Q8_0 ? 1LL : 2LL) * cus;
+  const int64_t target_wg = (S > 1 ? 2LL : 1LL) * cus;
   int64_t ns = (target_wg + base - 1) / base;
   const int min_pages = 8;
   const int64_t cap = (max_pages + min_pages - 1) / min_pages;
