@@ -86,33 +86,6 @@ __device__ __forceinline__ void pin4(f4_t &v) {
   v = f4_t{a0, a1, a2, a3};
 }
 
-// Two P' values of one scale group, split for f16 MFMA operands: with s0, s1 the fp16 scales
-// in the low / high half of `s2`, hi = (f16(p0*s0), f16(p1*s1)) and lo = (f16(p0*s0 - hi0),
-// f16(p1*s1 - hi1)); each is one fused multiply-add rounded once to f16 (v_fma_mix{lo,hi}_f16).
-__device__ __forceinline__ void pprime2(float p0, float p1, uint32_t s2, uint32_t &hi, uint32_t &lo) {
-  // One asm block: the first instruction of each pair defines the low half, the second the
-  // high half.  The trailing s_nop gives the two wait states an MFMA that reads hi or lo next
-  // needs after a VALU write (the compiler does not account for writes made inside asm).
-  // hi / lo are early-clobber: they are written while the inputs are still being read.
-  uint32_t h, l;
-  asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[0,1,0]\n\t"
-      "v_fma_mixhi_f16 %0, %3, %4, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
-      "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,1,1]\n\t"
-      "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]\n\t"
-      "s_nop 1"
-      : "=&v"(h), "=&v"(l)
-      : "v"(p0), "v"(p1), "v"(s2));
-  hi = h;
-  lo = l;
-}
-
-// fp16 number e of a lane's scale block (packed in 16-byte words).
-template <int N>
-__device__ __forceinline__ float scale_at(const u4_t (&w)[N], int e) {
-  const uint32_t d = w[e >> 3][(e >> 1) & 3];
-  return f16_bits_to_f32((e & 1) ? (d >> 16) : (d & 0xFFFFu));
-}
-
 // ------------------------------------------------------------------ quantize-on-write
 
 // The fp16 scale of a group with maximum magnitude amax: fp16(min(amax / 127, 65504)), an fp32
@@ -218,24 +191,19 @@ __global__ __launch_bounds__(256) void kv_write_bf16_kernel(WriteArgs a) {
 // ------------------------------------------------------------------ decode: split partials
 //
 // Workgroup (split j, KV head h, sequence s) of NW wavefronts.  The split owns pages
-// [j*cpp, min((j+1)*cpp, ceil(L/16))); the waves take units round-robin (INT8: 2 pages per
-// unit, BF16: 1 page).  Within a wavefront, lane l = 16*q4 + n16:
+// [j*cpp, min((j+1)*cpp, ceil(L/16))); the waves take its pages round-robin, one page per
+// unit.  Within a wavefront, lane l = 16*q4 + n16:
 //   Q.K   (A = K codes, B = Q):   lane holds scores of head n16, tokens 4*q4 .. 4*q4+3
-//   P.V   (A = P',      B = V):   A lane holds P' of head n16 for K-slots (page pg, token
-//                                 4*q4 + i) at element 4*pg + i -- the Q.K result layout
+//   P.V   (A = P',      B = V):   A lane holds P' of head n16 for tokens 4*q4 .. 4*q4+3 (the
+//                                 Q.K result layout), as f16 hi and lo parts
 //   acc   (P.V result):           lane holds heads 4*q4 .. 4*q4+3 of channel 16*jt + n16
-// Per unit: Q.K for the unit's pages, one softmax update (running max m, sum l, base 2), then
-// P.V; the accumulator is rescaled only when some head's maximum grew.  The next unit's
-// loads are issued as soon as the current unit's K (then V) registers are consumed.
+// Per page: Q.K, one softmax update (running max m, sum l, base 2), then P.V; the accumulator
+// is rescaled only when some head's maximum grew.  A page's loads are issued as soon as the
+// register buffer it lands in has been read out.
 // Each split writes an unnormalised partial o = sum_t 2^(x_t - m) v_t with m = max_t x_t,
 // x_t = log2(e) * q.k_t / sqrt(D), and l = sum_t 2^(x_t - m).
 
 typedef short s4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f4_t mfma16_f16(h4_t a, h4_t b, f4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
 
 // Register buffers (pages in flight + the page being processed) of the INT8 split kernel.
 constexpr int kI8Buffers = 2;
@@ -258,9 +226,6 @@ __device__ __forceinline__ float rows_sum(float x) {
 // 2^x for x <= 0 (softmax weights); results below 2^-126 may flush to zero, which is far
 // below fp32 resolution next to the largest weight (1).
 __device__ __forceinline__ float exp2_w(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// s_waitcnt immediate for vmcnt(n) alone (expcnt and lgkmcnt left at their maxima).
-__host__ __device__ constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // Buffer resource of one page or scale tile: loads past `bytes` return zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void *base, int64_t index, int bytes,
