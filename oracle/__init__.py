@@ -186,6 +186,25 @@ def decode(cache: OracleCache, q_bf16: np.ndarray, block_tables: np.ndarray, con
     return out, lse
 
 
+def decode_mq(cache: OracleCache, q_bf16: np.ndarray, block_tables: np.ndarray, context_lens: np.ndarray):
+    """Decode attention for n_q query tokens per sequence, causal among them, in fp64.
+
+    q_bf16 [S][n_q][Hq][D]: the queries of the last n_q positions L-n_q .. L-1 of sequence s
+    (L = context_lens[s]).  Query token i attends to the keys at positions 0 .. L-n_q+i, which is
+    ordinary decode attention over the first L-n_q+i+1 tokens; that is how it is computed here
+    (each query token is a sequence of its own with that context length and the same block
+    table).  Returns (out [S][n_q][Hq][D], lse [S][n_q][Hq]); a query with no visible key gives
+    out 0 and lse -inf.
+    """
+    q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+    S, nq, Hq, D = q.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    lens = (cl[:, None] - nq + 1 + np.arange(nq, dtype=np.int32)[None, :]).clip(min=0).astype(np.int32)
+    out, lse = decode(cache, q.reshape(S * nq, Hq, D), np.repeat(bt, nq, axis=0), lens.reshape(-1))
+    return out.reshape(S, nq, Hq, D), lse.reshape(S, nq, Hq)
+
+
 def dequantized_rows(cache: OracleCache, which: str) -> np.ndarray:
     """Decoded K or V of every (block, head, offset) in fp64: code * scale, or the bf16 value."""
     if cache.dtype == "int8":

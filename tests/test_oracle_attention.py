@@ -242,3 +242,89 @@ def test_row_subset_matches_full():
     rows = np.array([0, 5, 9, 23, 17], dtype=np.int64)
     o2, l2 = O.decode(cache, q, bt, lens, rows=rows)
     assert np.array_equal(o2, out.reshape(-1, 128)[rows]) and np.array_equal(l2, lse.reshape(-1)[rows])
+
+
+# ------------------------------------------------------------------ several query tokens
+
+def _bruteforce_mq(cache, q, bt, lens):
+    """Causal attention written out directly: the score matrix of the n_q queries against every
+    key of the context, with the keys after each query's position masked."""
+    K, V = _decoded(cache, "k"), _decoded(cache, "v")
+    S, nq, Hq, D = q.shape
+    G = Hq // cache.num_kv_heads
+    qf = bf16_bits_to_f32(q).astype(np.float64)
+    out = np.zeros((S, nq, Hq, D))
+    lse = np.full((S, nq, Hq), -np.inf)
+    for s in range(S):
+        L = int(lens[s])
+        if L == 0:
+            continue
+        t = np.arange(L)
+        blk, off = bt[s, t // PAGE], t % PAGE
+        pos = L - nq + np.arange(nq)                          # position of each query token
+        visible = t[None, :] <= pos[:, None]                  # [nq][L]
+        for hq in range(Hq):
+            Kt, Vt = K[blk, hq // G, off], V[blk, hq // G, off]
+            z = qf[s, :, hq] @ Kt.T / np.sqrt(D)              # [nq][L]
+            z = np.where(visible, z, -np.inf)
+            for i in range(nq):
+                if not visible[i].any():
+                    continue
+                m = z[i].max()
+                w = np.exp(z[i] - m)
+                out[s, i, hq] = (w @ Vt) / w.sum()
+                lse[s, i, hq] = m + np.log(w.sum())
+    return out, lse
+
+
+def _q_mq(seed, S, nq, Hq, D):
+    rng = np.random.default_rng(seed)
+    return f32_to_bf16_bits(rng.standard_normal((S, nq, Hq, D)).astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype", ["int8", "bf16"])
+def test_multi_token_bruteforce(dtype):
+    for seed, lens, Hq, Hkv, D, nq in [(21, [37, 70], 6, 1, 64, 3), (22, [16, 17, 5], 8, 4, 128, 5),
+                                       (23, [40], 4, 2, 256, 16)]:
+        cache, _, bt, lens = _problem(seed, lens, Hq, Hkv, D, dtype)
+        q = _q_mq(seed, len(lens), nq, Hq, D)
+        out, lse = O.decode_mq(cache, q, bt, lens)
+        ref, rlse = _bruteforce_mq(cache, q, bt, lens)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+        assert np.array_equal(np.isinf(lse), np.isinf(rlse))
+        fin = np.isfinite(rlse)
+        assert np.allclose(lse[fin], rlse[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_multi_token_one_query_is_decode():
+    cache, q1, bt, lens = _problem(24, [300, 33], 6, 2, 64, "int8")
+    out, lse = O.decode_mq(cache, q1[:, None], bt, lens)
+    ref, rlse = O.decode(cache, q1, bt, lens)
+    assert np.array_equal(out[:, 0], ref) and np.array_equal(lse[:, 0], rlse)
+
+
+def test_multi_token_is_causal():
+    """Changing the last token's key and value changes only the last query's output."""
+    cache, _, bt, lens = _problem(25, [90], 6, 2, 64, "int8")
+    q = _q_mq(25, 1, 4, 6, 64)
+    out, _ = O.decode_mq(cache, q, bt, lens)
+    rng = np.random.default_rng(26)
+    L = int(lens[0])
+    slot = np.array([bt[0, (L - 1) // PAGE] * PAGE + (L - 1) % PAGE], np.int32)
+    O.kv_write(cache, f32_to_bf16_bits(rng.standard_normal((1, 2, 64)).astype(np.float32) * 5),
+               f32_to_bf16_bits(rng.standard_normal((1, 2, 64)).astype(np.float32) * 5), slot)
+    out2, _ = O.decode_mq(cache, q, bt, lens)
+    assert np.array_equal(out[:, :3], out2[:, :3])
+    assert not np.allclose(out[:, 3], out2[:, 3])
+
+
+def test_multi_token_more_queries_than_context():
+    """Query tokens before the first position see no key: out 0, lse -inf."""
+    cache, _, bt, lens = _problem(27, [3, 0], 4, 2, 32, "int8")
+    q = _q_mq(27, 2, 5, 4, 32)
+    out, lse = O.decode_mq(cache, q, bt, lens)
+    assert np.all(out[0, :2] == 0) and np.all(np.isneginf(lse[0, :2]))
+    assert np.all(np.isfinite(lse[0, 2:]))
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+    ref, rlse = _bruteforce_mq(cache, q, bt, lens)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
