@@ -51,6 +51,7 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     p.add_argument("--no-bf16", action="store_true", help="skip the BF16-cache comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-multi-token", action="store_true", help="skip the several-query-token decode timings")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU seconds for the oracle sample")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     p.add_argument("--sweep", action="store_true",
@@ -152,6 +153,29 @@ def time_step(torch, step, steps, warmup, eager):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     return e0.elapsed_time(e1) / steps, wall
+
+
+def time_multi_token(torch, K, layers, S, Hq, D, mcl, lens, Hkv, n_layers, steps, warmup):
+    """us per step (every layer: split + merge) of decode with n_q query tokens per sequence,
+    causal among them, at the library's split count; graph replay as for the main step."""
+    res = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    for nq in (2, 4, 8):
+        q = torch.randn((S, nq, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+        ns = K.choose_num_splits_mq(layers[0].cache, S, nq, Hq, mcl)
+        ws = torch.empty(K.workspace_bytes(layers[0].cache, S * nq, Hq, ns), dtype=torch.uint8, device="cuda")
+        outs = [(torch.empty((S, nq, Hq, D), dtype=torch.float32, device="cuda"),
+                 torch.empty((S, nq, Hq), dtype=torch.float32, device="cuda")) for _ in layers]
+
+        def step():
+            for L, (o, l) in zip(layers, outs):
+                K.decode_mq(L.cache, q, L.bt, L.lens, mcl, ns, out=o, lse=l, workspace=ws)
+        ms, _ = time_step(torch, step, steps, warmup, False)
+        res[str(nq)] = {"us_per_step": round(ms * 1e3, 1), "num_splits": ns,
+                        "GB_per_s": round(algorithmic_bytes(lens, Hkv, D, "int8") * n_layers / (ms * 1e-3) / 1e9, 1)}
+        log(f"int8 decode with {nq} query tokens: {ms * 1e3:.1f} us/step, splits {ns}")
+    return res
 
 
 def sleep_cycles_for(torch, ms):
@@ -514,6 +538,9 @@ def main():
             "decode_split_us": round(b["kern_us"], 3),
             "int8_speedup_step": round(b["ms"] / r["ms"], 3),
         }
+    if not args.no_multi_token:
+        out["multi_token"] = time_multi_token(torch, K, states["int8"], S, Hq, D, mcl, lens, Hkv, n_layers,
+                                              args.steps, args.warmup)
     if not args.no_cpu_baseline:
         el, nb, nl, max_err, within = cpu_baseline(host, states["int8"], args.cpu_budget_s)
         import oracle as O

@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["Cache", "KvqError", "write", "decode", "decode_step", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
+__all__ = ["Cache", "KvqError", "write", "decode", "decode_mq", "choose_num_splits_mq", "decode_step", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
            "status_string", "lib", "LIB_PATH", "INT8", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -52,6 +52,10 @@ lib.kvq_decode_attention.restype = ctypes.c_int
 lib.kvq_check_decode.argtypes = _DEC
 lib.kvq_check_decode.restype = ctypes.c_int
 _STEP = [_CP, _P, _P] + _DEC[1:]
+lib.kvq_decode_attention_mq.argtypes = [_CP, _P, _i32] + _DEC[2:]
+lib.kvq_decode_attention_mq.restype = ctypes.c_int
+lib.kvq_choose_num_splits_mq.argtypes = [_CP, _i32, _i32, _i32, _i32]
+lib.kvq_choose_num_splits_mq.restype = _i32
 lib.kvq_decode_step.argtypes = _STEP
 lib.kvq_decode_step.restype = ctypes.c_int
 lib.kvq_check_decode_step.argtypes = _STEP
@@ -198,6 +202,42 @@ def decode(cache: Cache, q, block_tables, context_lens, max_context_len: int, nu
                                   workspace, want_lse)
     fn = lib.kvq_check_decode if checked else lib.kvq_decode_attention
     _check(fn(ctypes.byref(cache.desc), *args, _stream(stream)), "kvq_decode_attention")
+    return out, lse
+
+
+def choose_num_splits_mq(cache: Cache, num_seqs: int, num_query_tokens: int, num_q_heads: int,
+                         max_context_len: int) -> int:
+    r = int(lib.kvq_choose_num_splits_mq(ctypes.byref(cache.desc), num_seqs, num_query_tokens, num_q_heads,
+                                         max_context_len))
+    if r < 0:
+        raise KvqError(r, "kvq_choose_num_splits_mq")
+    return r
+
+
+def decode_mq(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int = 0, *,
+              out=None, lse=None, workspace=None, want_lse: bool = True, stream=None):
+    """Decode attention for q [S][n_q][Hq][D] bf16 (the last n_q positions of each sequence, causal
+    among them); returns (out fp32 [S][n_q][Hq][D], lse fp32 [S][n_q][Hq] or None)."""
+    q = _as_bits16(q)
+    S, nq, Hq, D = (int(x) for x in q.shape)
+    if D != cache.head_dim or not q.is_contiguous():
+        raise ValueError("q must be contiguous [S][n_q][Hq][D] bf16")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or block_tables.dim() != 2 \
+            or block_tables.shape[0] != S or context_lens.shape != (S,) \
+            or not (block_tables.is_contiguous() and context_lens.is_contiguous()):
+        raise ValueError("int32 block_tables [S][max_blocks] and context_lens [S] required")
+    ns = num_splits if num_splits else choose_num_splits_mq(cache, S, nq, Hq, max_context_len)
+    if out is None:
+        out = torch.empty((S, nq, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((S, nq, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(cache, S * nq, Hq, ns), 256), dtype=torch.uint8, device=q.device)
+    st = lib.kvq_decode_attention_mq(ctypes.byref(cache.desc), _ptr(q), nq, _ptr(block_tables),
+                                     int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), S, Hq,
+                                     int(ns), _ptr(out), _ptr(lse), _ptr(workspace),
+                                     int(workspace.numel() * workspace.element_size()), _stream(stream))
+    _check(st, "kvq_decode_attention_mq")
     return out, lse
 
 

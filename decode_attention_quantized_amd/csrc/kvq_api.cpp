@@ -59,13 +59,15 @@ int device_cus() {
 // workgroup per CU evens out the longest ones (the host sees only the maximum length).  Both
 // choices come from split-count sweeps of the INT8 and BF16 kernels on 256 CUs (one sequence at
 // 4K and 32K tokens, 4 sequences of 2K-32K, 32 sequences of 512-8K).
-int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus) {
+// (row_tiles > 1: several query tokens per sequence, one workgroup per 16-row tile of (query
+// token, head) pairs; the tiles of one split count as a batch.)
+int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus, int row_tiles = 1) {
   (void)dtype;
   (void)D;
   const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
   if (max_pages <= 0) return 1;
-  const int64_t base = (int64_t)S * Hkv;
-  const int64_t target_wg = (S > 1 ? 2LL : 1LL) * cus;
+  const int64_t base = (int64_t)S * Hkv * row_tiles;
+  const int64_t target_wg = ((int64_t)S * row_tiles > 1 ? 2LL : 1LL) * cus;
   int64_t ns = (target_wg + base - 1) / base;
   const int min_pages = 8;
   const int64_t cap = (max_pages + min_pages - 1) / min_pages;
@@ -98,14 +100,20 @@ bool bf16_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
 
 // Validates the decode arguments and fills the kernel argument block; no HIP call is made
 // unless num_splits == 0 (the heuristic reads the device's compute-unit count).
+constexpr int kMaxQueryTokens = 64;
+
+int row_tiles_for(int nq, int G) { return nq > 1 ? (nq * G + 15) / 16 : 1; }
+
 int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
                    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                    int32_t num_splits, float *out, float *lse, const void *workspace, size_t workspace_bytes_given,
-                   bool need_inputs, bool need_outputs, kvq::DecodeArgs &a) {
+                   bool need_inputs, bool need_outputs, kvq::DecodeArgs &a, int nq = 1) {
   int st = check_cache(cache);
   if (st != KVQ_OK) return st;
   st = check_heads(cache, num_q_heads);
   if (st != KVQ_OK) return st;
+  if (nq < 1 || nq > kMaxQueryTokens) return KVQ_ERR_INVALID_ARG;
+  if (nq > 1 && cache->dtype != KVQ_INT8_Q8_0) return KVQ_ERR_UNSUPPORTED;
   if (num_seqs <= 0 || (need_inputs && max_blocks_per_seq <= 0)) return KVQ_ERR_INVALID_ARG;
   if (max_context_len < 1 || (need_inputs && (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage))
     return KVQ_ERR_INVALID_ARG;
@@ -114,10 +122,15 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   if (need_inputs && (!q || !block_tables || !aligned(q, 16) || !aligned(block_tables, 4))) return KVQ_ERR_INVALID_ARG;
   if (need_outputs && (!out || !aligned(out, 16) || (lse && !aligned(lse, 4)))) return KVQ_ERR_INVALID_ARG;
   const int D = cache->head_dim, Hkv = cache->num_kv_heads;
-  const int NS = num_splits ? num_splits : choose_splits(cache->dtype, num_seqs, Hkv, D, max_context_len, device_cus());
-  if ((int64_t)num_seqs * Hkv * NS > INT32_MAX || (int64_t)num_seqs * num_q_heads * (D / 64) > INT32_MAX)
+  const int RT = row_tiles_for(nq, num_q_heads / Hkv);
+  const int NS = num_splits ? num_splits
+                            : choose_splits(cache->dtype, num_seqs, Hkv, D, max_context_len, device_cus(), RT);
+  if ((int64_t)num_seqs * Hkv * NS * RT > INT32_MAX || (int64_t)num_seqs * nq * num_q_heads * (D / 64) > INT32_MAX)
     return KVQ_ERR_INVALID_ARG;
-  if (workspace_bytes_given < workspace_bytes(num_seqs, num_q_heads, NS, D)) return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  // one sequence's query block and partials are addressed with 32-bit buffer offsets
+  if (nq > 1 && ((int64_t)nq * num_q_heads * NS * D * 4 >= INT32_MAX || (int64_t)nq * num_q_heads * D * 2 >= INT32_MAX))
+    return KVQ_ERR_INVALID_ARG;
+  if (workspace_bytes_given < workspace_bytes(num_seqs * nq, num_q_heads, NS, D)) return KVQ_ERR_WORKSPACE_TOO_SMALL;
   const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
   a.q = static_cast<const uint16_t *>(q);
   a.kc = cache->k;
@@ -126,7 +139,7 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   a.vs = static_cast<const uint16_t *>(cache->v_scales);
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  const size_t rows = (size_t)num_seqs * num_q_heads * NS;
+  const size_t rows = (size_t)num_seqs * nq * num_q_heads * NS;
   const size_t o_bytes = (rows * D * sizeof(float) + 255) & ~(size_t)255;
   a.o_part = static_cast<float *>(const_cast<void *>(workspace));
   a.ml = reinterpret_cast<float2 *>(static_cast<char *>(const_cast<void *>(workspace)) + o_bytes);
@@ -145,6 +158,8 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   a.cpp = (max_pages + NS - 1) / NS;
   a.D = D;
   a.waves = waves_for(cache->dtype, D);
+  a.nq = nq;
+  a.row_tiles = RT;
   return KVQ_OK;
 }
 
@@ -292,6 +307,33 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          void *workspace, size_t workspace_bytes_given, void *stream) {
   return decode_impl(cache, nullptr, nullptr, q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
                      num_seqs, num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+}
+
+int kvq_decode_attention_mq(const kvq_cache_t *cache, const void *q, int32_t num_query_tokens,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                            float *out, float *lse, void *workspace, size_t workspace_bytes_given, void *stream) {
+  kvq::DecodeArgs a;
+  int st = prepare_decode(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, true, true, a,
+                          num_query_tokens);
+  if (st != KVQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kvq::launch_decode_split(cache->dtype, a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
+  if (kvq::launch_decode_merge(a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
+  return KVQ_OK;
+}
+
+int32_t kvq_choose_num_splits_mq(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_query_tokens,
+                                 int32_t num_q_heads, int32_t max_context_len) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = check_heads(cache, num_q_heads);
+  if (st != KVQ_OK) return st;
+  if (num_seqs <= 0 || max_context_len < 1 || num_query_tokens < 1 || num_query_tokens > kMaxQueryTokens)
+    return KVQ_ERR_INVALID_ARG;
+  return choose_splits(cache->dtype, num_seqs, cache->num_kv_heads, cache->head_dim, max_context_len, device_cus(),
+                       row_tiles_for(num_query_tokens, num_q_heads / cache->num_kv_heads));
 }
 
 int kvq_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,

@@ -28,6 +28,8 @@ struct DecodeArgs {
                                   // into its page by the split kernel before the page is read (or null)
   int max_blocks, max_context_len, S, Hq, Hkv, G, NB, NS, cpp, D;
   int waves;                      // wavefronts per split workgroup (1, 2, 4 or 8)
+  int nq;                         // query tokens per sequence (q [S][nq][Hq][D], causal among them)
+  int row_tiles;                  // ceil(nq * G / 16): 16-row MFMA tiles of (query token, head) pairs
 };
 
 // Each returns hipSuccess or the launch error.  dtype: 0 INT8, 1 BF16.

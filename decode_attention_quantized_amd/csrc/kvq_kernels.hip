@@ -335,6 +335,20 @@ __device__ __forceinline__ void write_new_bf16(const DecodeArgs &a, int64_t page
   }
 }
 
+// Q operand for several query tokens: MFMA row r = 16 * rt + n16 of KV head h is the pair
+// (query token r / G, head h * G + r % G); rows past nq * G read zeros.
+template <int D>
+__device__ __forceinline__ void load_q_mq(const DecodeArgs &a, int s, int h, int rt, int n16, int q4,
+                                          u4_t (&qraw)[D / 32]) {
+  const uint16_t *base = a.q + (int64_t)s * a.nq * a.Hq * D;
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, a.nq * a.Hq * D * 2, 0x00020000);
+  const int row = 16 * rt + n16;
+  const int i = row / a.G, g = row - i * a.G;
+  const int off = row < a.nq * a.G ? (((i * a.Hq + h * a.G + g) * D) + 8 * q4) * 2 : 0x40000000;
+#pragma unroll
+  for (int gg = 0; gg < D / 32; ++gg) qraw[gg] = ld16(r, off, gg * kGroup * 2);
+}
+
 // Merge scratch of one wave (floats): its accumulator tiles as [tile][lane][4], then m[16]
 // and l[16].
 template <int D>
@@ -344,15 +358,17 @@ constexpr int merge_stride() { return (D / 16) * 256 + 32; }
 // merge; `merge` holds NW regions of merge_stride<D>() floats).  Every wave stores its
 // accumulator tiles as they sit in its registers; wave w then combines tiles w, w + NW, ...
 // of all waves for its own lanes' rows, each wave's rows weighted by 2^(m_w - M).
-template <int D, int NW>
+template <int D, int NW, bool MQ = false>
 __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h, int j, int wave, int n16, int q4,
-                                              float m_run, float l_run, const f4_t (&acc)[D / 16], float *merge) {
+                                              float m_run, float l_run, const f4_t (&acc)[D / 16], float *merge,
+                                              int rt = 0) {
   constexpr int NT = D / 16;
   constexpr int ST = merge_stride<D>();
   const int G = a.G;
   const int lane = q4 * 16 + n16;
   l_run = rows_sum(l_run);
   const int64_t row0 = ((int64_t)s * a.Hq + (int64_t)h * G) * a.NS + j;  // partial of head h*G + 0
+  static_assert(!(MQ && NW == 1), "several query tokens use the LDS merge path");
   if constexpr (NW == 1) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt)
@@ -364,7 +380,8 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
     if (q4 == 0 && n16 < G) a.ml[row0 + (int64_t)n16 * a.NS] = make_float2(m_run, l_run);
   } else {
     float *mine = merge + wave * ST;
-    if (4 * q4 < G) {  // lanes that hold a real head
+    const int rows_here = MQ ? min(a.nq * G - 16 * rt, 16) : G;  // real rows of this tile
+    if (4 * q4 < rows_here) {  // lanes that hold a real row
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) *reinterpret_cast<f4_t *>(mine + (jt * 64 + lane) * 4) = acc[jt];
     }
@@ -394,15 +411,39 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
         Lsum[i] = fmaf(wt[w][i], lw[i], Lsum[i]);
       }
     }
-    const int rows_valid = (G - 1) * a.NS + 1;  // rows from head 0 through head G - 1 of this split
+    // row_off[i]: offset (in partial rows) of this lane's row 4 q4 + i from the resources' base;
+    // rows past the end of the resources are dropped by the bounds check
+    int row_off[4];
+    int rows_valid;
+    const float2 *ml_base;
+    const float *o_base;
+    if constexpr (MQ) {
+      // tile row 16 rt + r is (query token (16 rt + r) / G, head h G + (16 rt + r) % G) of sequence s
+      const int64_t seq0 = (int64_t)s * a.nq * a.Hq * a.NS;  // first partial row of the sequence
+      rows_valid = a.nq * a.Hq * a.NS;
+      ml_base = a.ml + seq0;
+      o_base = a.o_part + seq0 * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * rt + 4 * q4 + i;
+        const int t = row / G, g = row - t * G;
+        row_off[i] = row < a.nq * G ? (t * a.Hq + h * G + g) * a.NS + j : rows_valid;
+      }
+    } else {
+      rows_valid = (G - 1) * a.NS + 1;  // rows from head 0 through head G - 1 of this split
+      ml_base = a.ml + row0;
+      o_base = a.o_part + row0 * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) row_off[i] = (4 * q4 + i) * a.NS;
+    }
     if (wave == 0 && n16 == 0) {
-      const auto rml = __builtin_amdgcn_make_buffer_rsrc(a.ml + row0, 0, rows_valid * 8, 0x00020000);
+      const auto rml = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2 *>(ml_base), 0, rows_valid * 8, 0x00020000);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(u2_t, make_float2(M[i], Lsum[i])), rml, (4 * q4 + i) * a.NS * 8, 0, 0);
+            __builtin_bit_cast(u2_t, make_float2(M[i], Lsum[i])), rml, row_off[i] * 8, 0, 0);
     }
-    const auto ro = __builtin_amdgcn_make_buffer_rsrc(a.o_part + row0 * D, 0, rows_valid * D * 4, 0x00020000);
+    const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o_base), 0, rows_valid * D * 4, 0x00020000);
     f4_t o[NT / NW];
 #pragma unroll
     for (int t = 0; t < NT / NW; ++t) {  // every LDS read is issued before the first store
@@ -420,7 +461,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[t][i]), ro,
-                                              ((4 * q4 + i) * a.NS * D + 16 * (wave + t * NW) + n16) * 4, 0, 0);
+                                              (row_off[i] * D + 16 * (wave + t * NW) + n16) * 4, 0, 0);
   }
 }
 
@@ -428,9 +469,9 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
 //
 // A wave owns pages p0 + wave + k * NW (k = 0, 1, ...) of its split.  Page k lands in register
 // buffer k % NBUF; the page is requested as soon as its buffer has been read out, so while the
-// wave works on one page the next NBUF - 1 are in flight.  Q and the first page's K are
-// requested before anything else.
-template <int D, int NW>
+// wave works on one page the next NBUF - 1 are in flight.  Q and the first page are requested
+// before anything else; the other buffers fill once Q has arrived.
+template <int D, int NW, bool MQ>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
   constexpr int NG = D / kGroup;      // scale groups
@@ -449,8 +490,10 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
   const int n16 = lane & 15, q4 = lane >> 4;
   const int j = blockIdx.x % a.NS;
-  const int h = (blockIdx.x / a.NS) % a.Hkv;
-  const int s = blockIdx.x / (a.NS * a.Hkv);
+  // (MQ: the workgroup's 16-row tile of (query token, head) pairs, between split and KV head)
+  const int rt = MQ ? (blockIdx.x / a.NS) % a.row_tiles : 0;
+  const int h = (blockIdx.x / (a.NS * (MQ ? a.row_tiles : 1))) % a.Hkv;
+  const int s = blockIdx.x / (a.NS * (MQ ? a.row_tiles : 1) * a.Hkv);
   const int L = max(0, min(context_lens[s], a.max_context_len));
   const int P = (L + kPage - 1) / kPage;
   const int p0 = j * a.cpp;
@@ -494,10 +537,15 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   // The wave that holds the sequence's last page writes the step's new token into it first (its
   // local page index k_last; written before that page is requested).
   const int blk_last = btrow[P - 1];
-  const bool own_new = a.k_new != nullptr && p1 == P && wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
+  const bool own_new =
+      !MQ && a.k_new != nullptr && p1 == P && wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
   const int k_last = (n_units - 1) / NW;
+  // MQ: the lane's row sees keys 0 .. L - nq + token (causal among the query tokens)
+  int L_row = L;
+  if constexpr (MQ) L_row = L - a.nq + (16 * rt + n16) / a.G + 1;
   u4_t qraw[NG];
-  load_q<D>(a, s, h, n16, q4, qraw);
+  if constexpr (MQ) load_q_mq<D>(a, s, h, rt, n16, q4, qraw);
+  else load_q<D>(a, s, h, n16, q4, qraw);
   u2_t knew, vnew;
   load_new_rows<D>(a, s, h, own_new, lane, knew, vnew);
   __builtin_amdgcn_sched_barrier(0);
@@ -505,6 +553,8 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   const int t_new = (L - 1) & (kPage - 1);
   if (own_new && k_last == 0) write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
   issue_k(0, 0, blk[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  issue_v(0, 0, blk[0]);
   __builtin_amdgcn_sched_barrier(0);
 
   // Q: bf16 rescaled by 2^shift per head so that max |q| lies in [2^14, 2^15): exact in f16.
@@ -542,9 +592,6 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   }
   const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
   if (own_new && k_last != 0) write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
-  // (scheduling barriers keep the loads in this order: the compiler's wait counts follow it)
-  issue_v(0, 0, blk[0]);
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 1; b < NBUF; ++b) {
     issue_k(b, b, blk[b]);
@@ -612,8 +659,10 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     // ---- online softmax over the page's 16 tokens (base 2).  Padding heads (Q = 0) get finite
     // scores; their rows are never written out.
     float x[4];
+    int lim_row = lim;  // valid tokens of the page for this lane's row
+    if constexpr (MQ) lim_row = u < n_units ? min(max(L_row - (p0 + u) * kPage, 0), kPage) : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim) ? sc[i] * cmul : -INFINITY;
+    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim_row) ? sc[i] * cmul : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -686,7 +735,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       blk_next = block_of(k + b + NBUF + 1);
     }
   }
-  write_partial<D, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge);
+  write_partial<D, NW, MQ>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, rt);
 }
 
 // ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
@@ -818,7 +867,8 @@ void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_ta
 
 // ------------------------------------------------------------------ decode: merge
 //
-// Workgroup (64-channel chunk, query head, sequence) of kMergeWaves wavefronts; wave w takes
+// Workgroup (64-channel chunk, output row, sequence) of kMergeWaves wavefronts (an output row is a
+// (query token, query head) pair; one query token per sequence unless nq > 1); wave w takes
 // splits w, w + kMergeWaves, ... and folds them into a running (m, l, o) with the same rescaling
 // as the online softmax, so the partials are read in one pass (no separate pass for the global
 // maximum).  Only the splits that hold pages are folded (their count follows from the context
@@ -832,11 +882,12 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
   constexpr int UNR = 16;  // partials requested together per wave (one round trip up to 64 splits)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int HQ = a.Hq * a.nq;  // output rows per sequence: (query token, query head)
   const int chunk = blockIdx.x % NCH;
-  const int hq = (blockIdx.x / NCH) % a.Hq;
-  const int s = blockIdx.x / (NCH * a.Hq);
+  const int hq = (blockIdx.x / NCH) % HQ;
+  const int s = blockIdx.x / (NCH * HQ);
   const int c = chunk * 64 + lane;
-  const int64_t orow = ((int64_t)s * a.Hq + hq);
+  const int64_t orow = ((int64_t)s * HQ + hq);
   const int64_t base = orow * a.NS;
 
   const int Lc = a.context_lens[s];  // (the loads below do not depend on it)
@@ -914,7 +965,8 @@ static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
   const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), smem, stream, a,
+                       a.block_tables);
   else
     hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
 }
@@ -929,8 +981,20 @@ static void launch_split_nw(const DecodeArgs &a, hipStream_t stream) {
   }
 }
 
+// Several query tokens per sequence (INT8 cache, 4 waves): one workgroup per (16-row tile, split,
+// KV head, sequence).
+template <int D>
+static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
+  const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.row_tiles * a.NS);
+  const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);
+  hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, true>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
+}
+
 hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t stream) {
-  if (dtype == 0) {
+  if (dtype == 0 && a.nq > 1) {
+    if (a.D == 256) launch_split_mq<256>(a, stream);
+    else launch_split_mq<128>(a, stream);
+  } else if (dtype == 0) {
     if (a.D == 256) launch_split_nw<256, true>(a, stream);
     else launch_split_nw<128, true>(a, stream);
   } else {
@@ -941,7 +1005,7 @@ hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t strea
 }
 
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
-  const unsigned grid = (unsigned)((int64_t)a.S * a.Hq * (a.D / 64));
+  const unsigned grid = (unsigned)((int64_t)a.S * a.Hq * a.nq * (a.D / 64));
   if (a.D == 256) hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, a);
   else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, a);
   return hipGetLastError();

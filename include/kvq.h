@@ -21,6 +21,11 @@
  *                        section "Read the compressed cache without copying it first": one
  *                        query token reads the int8 cache directly, V dequantized in registers,
  *                        no converted copy of the cache.
+ *   kvq_decode_attention_mq  several query tokens per sequence (multi-token decode, for example
+ *                        checking drafted tokens), causal among them.  Half-the-memory page, section
+ *                        "The stock path was slow" and the request-performance sections: steps
+ *                        that generate or check up to 16 tokens per request run on the INT8
+ *                        kernel; each query token attends to the cache up to its own position.
  *   kvq_decode_step      one decode step of one layer in a single kernel pass: the new token's
  *                        quantize-on-write (as kvq_write) fused into the split kernel, then the
  *                        merge (as kvq_decode_attention).  Gllm page, section "Interpretation":
@@ -154,6 +159,31 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
                          int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Decode attention for num_query_tokens (n_q, 1..64) query tokens per sequence, causal among them
+ * (INT8 cache only).  The query tokens of sequence s are its last n_q positions L-n_q .. L-1
+ * (L = context_lens[s], which includes them): query token i attends to the keys at positions
+ * 0 .. L-n_q+i.  n_q == 1 is kvq_decode_attention.
+ *   q            device, bfloat16 [num_seqs][n_q][num_q_heads][D], 16-byte aligned.
+ *   out          device, fp32 [num_seqs][n_q][num_q_heads][D].
+ *   lse          device, fp32 [num_seqs][n_q][num_q_heads], or NULL.
+ *   workspace    at least kvq_decode_workspace_bytes(cache, num_seqs * n_q, num_q_heads, splits)
+ *                bytes, where splits is num_splits or, for 0, kvq_choose_num_splits_mq(...).
+ *   other arguments as kvq_decode_attention.  A query token with no visible key (L < n_q) gets
+ *   out = 0 and lse = -inf.  Returns KVQ_ERR_UNSUPPORTED for a BF16 cache with n_q > 1.
+ * The (query token, head) pairs of one KV head form the rows of the MFMA tiles: n_q * G <= 16
+ * costs the same cache reads as one query token; beyond that each further 16 rows read the
+ * sequence's pages again.
+ */
+int kvq_decode_attention_mq(const kvq_cache_t *cache, const void *q, int32_t num_query_tokens,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                            float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Split count kvq_decode_attention_mq uses for num_splits == 0 (negative status on error). */
+int32_t kvq_choose_num_splits_mq(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_query_tokens,
+                                 int32_t num_q_heads, int32_t max_context_len);
 
 /*
  * One decode step: writes the new token of every sequence into the cache, then attention and

@@ -136,6 +136,23 @@ def test_decode_step_rejects_invalid_arguments():
                                        None, FAKE, 1 << 30, None) == -1
 
 
+def test_decode_mq_rejects_invalid_arguments():
+    d = _desc()
+
+    def mq(desc, nq=2, q=FAKE, Hq=24, ns=4, wsb=1 << 30):
+        return K.lib.kvq_decode_attention_mq(ctypes.byref(desc), q, nq, FAKE, 32, FAKE, 512, 1, Hq, ns, FAKE, None,
+                                             FAKE, wsb, None)
+    assert mq(d, nq=0) == -1
+    assert mq(d, nq=65) == -1
+    assert mq(d, q=None) == -1
+    assert mq(d, Hq=25) == -1
+    assert mq(_desc(dtype=K.BF16, ks=None, vs=None)) == -2      # INT8 cache only for n_q > 1
+    need = K.lib.kvq_decode_workspace_bytes(ctypes.byref(d), 1 * 2, 24, 4)
+    assert mq(d, wsb=need - 1) == -3                            # rows = num_seqs * n_q * Hq
+    assert K.lib.kvq_choose_num_splits_mq(ctypes.byref(d), 1, 0, 24, 512) == -1
+    assert 1 <= K.lib.kvq_choose_num_splits_mq(ctypes.byref(d), 1, 4, 24, 32768) <= 4096
+
+
 def test_workspace_bytes_formula():
     d = _desc()
     for S, Hq, ns, D in [(1, 24, 64, 256), (32, 32, 7, 128), (4, 24, 256, 256)]:
