@@ -62,6 +62,10 @@ def lib():
         L.oracle_kv_write_bf16.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_decode_int8.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, i64, i32, i32, P, P]
         L.oracle_decode_bf16.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, i64, i32, i32, P, P]
+        L.oracle_kv_write_int8_head.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P]
+        L.oracle_decode_int8_head.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, i64, i32, i32,
+                                              P, P]
+        L.oracle_quantize_rows_f32.argtypes = [P, i64, i32, P, P]
         L.oracle_num_threads.restype = i32
         _lib = L
     return _lib
@@ -100,11 +104,22 @@ def quantize_groups(x_bf16) -> tuple[np.ndarray, np.ndarray]:
     return codes, scales
 
 
+def quantize_rows_head(x_bf16) -> tuple[np.ndarray, np.ndarray]:
+    """Per-head format: rows of D bf16 values (last axis) -> (int8 codes [..., D], fp32 scales [...])."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    n = x.shape[-1]
+    assert 0 < n <= 256
+    codes = np.empty(x.shape, dtype=np.int8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    lib().oracle_quantize_rows_f32(_p(x), x.size // n, n, _p(codes), _p(scales))
+    return codes, scales
+
+
 # ------------------------------------------------------------------ cache images
 
 @dataclass
 class OracleCache:
-    dtype: str               # "int8" or "bf16"
+    dtype: str               # "int8" (q8_0: fp16 scale per 32 values), "int8_head" (fp32 scale per row) or "bf16"
     num_blocks: int
     num_kv_heads: int
     head_dim: int
@@ -124,6 +139,10 @@ class OracleCache:
             sshape = (num_blocks, num_kv_heads, PAGE, head_dim // GROUP)
             ks = np.full(sshape, scale_fill, dtype=np.uint16)
             return OracleCache(dtype, num_blocks, num_kv_heads, head_dim, k, v, ks, ks.copy())
+        if dtype == "int8_head":  # poison scale: the largest finite fp32
+            k = np.full(shape, np.int8(np.uint8(code_fill).view(np.int8)), dtype=np.int8)
+            ks = np.full((num_blocks, num_kv_heads, PAGE), np.finfo(np.float32).max, dtype=np.float32)
+            return OracleCache(dtype, num_blocks, num_kv_heads, head_dim, k, k.copy(), ks, ks.copy())
         if dtype == "bf16":
             k = np.full(shape, bf16_fill, dtype=np.uint16)
             return OracleCache(dtype, num_blocks, num_kv_heads, head_dim, k, k.copy())
@@ -141,6 +160,9 @@ def kv_write(cache: OracleCache, k_bf16: np.ndarray, v_bf16: np.ndarray, slot_ma
     if cache.dtype == "int8":
         L.oracle_kv_write_int8(T, cache.num_kv_heads, cache.head_dim, cache.num_blocks, _p(k), _p(v), _p(sm),
                                _p(cache.k), _p(cache.v), _p(cache.k_scales), _p(cache.v_scales))
+    elif cache.dtype == "int8_head":
+        L.oracle_kv_write_int8_head(T, cache.num_kv_heads, cache.head_dim, cache.num_blocks, _p(k), _p(v), _p(sm),
+                                    _p(cache.k), _p(cache.v), _p(cache.k_scales), _p(cache.v_scales))
     else:
         L.oracle_kv_write_bf16(T, cache.num_kv_heads, cache.head_dim, cache.num_blocks, _p(k), _p(v), _p(sm),
                                _p(cache.k), _p(cache.v))
@@ -178,6 +200,10 @@ def decode(cache: OracleCache, q_bf16: np.ndarray, block_tables: np.ndarray, con
         L.oracle_decode_int8(S, Hq, cache.num_kv_heads, D, cache.num_blocks, bt.shape[1], _p(q), _p(bt), _p(cl),
                              _p(cache.k), _p(cache.v), _p(cache.k_scales), _p(cache.v_scales), rp, n,
                              num_splits, max_context_len, _p(out), _p(lse))
+    elif cache.dtype == "int8_head":
+        L.oracle_decode_int8_head(S, Hq, cache.num_kv_heads, D, cache.num_blocks, bt.shape[1], _p(q), _p(bt),
+                                  _p(cl), _p(cache.k), _p(cache.v), _p(cache.k_scales), _p(cache.v_scales), rp, n,
+                                  num_splits, max_context_len, _p(out), _p(lse))
     else:
         L.oracle_decode_bf16(S, Hq, cache.num_kv_heads, D, cache.num_blocks, bt.shape[1], _p(q), _p(bt), _p(cl),
                              _p(cache.k), _p(cache.v), rp, n, num_splits, max_context_len, _p(out), _p(lse))
@@ -211,6 +237,10 @@ def dequantized_rows(cache: OracleCache, which: str) -> np.ndarray:
         codes = cache.k if which == "k" else cache.v
         sc = f16_to_f32(cache.k_scales if which == "k" else cache.v_scales).astype(np.float64)
         return codes.astype(np.float64) * np.repeat(sc, GROUP, axis=-1)
+    if cache.dtype == "int8_head":
+        codes = cache.k if which == "k" else cache.v
+        sc = (cache.k_scales if which == "k" else cache.v_scales).astype(np.float64)
+        return codes.astype(np.float64) * sc[..., None]
     arr = cache.k if which == "k" else cache.v
     return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 

@@ -29,10 +29,17 @@
  *     calculation": cut the context into segments, keep for each a weighted value sum and
  *     its normalisation terms, and combine with those terms (never by averaging).
  *
+ *   - the per-head format (oracle_quantize_row_f32, oracle_kv_write_int8_head): the
+ *     half-the-memory page, sections on vLLM's int8_per_token_head format and "Is 8 bits
+ *     enough?": every value of a (token, head) row as an 8-bit integer with one shared 32-bit
+ *     scale, 520 bytes per token per head at D = 256 (one scale per 256 values); the same
+ *     symmetric amax/127 rule, with the scale kept in fp32.
+ *
  * Cache images here use the LOGICAL layout (the GPU library stores the same bytes in a
  * permuted in-page order):
  *     codes  int8  [num_blocks][Hkv][16][D]
  *     scales fp16  [num_blocks][Hkv][16][D/32]   (raw IEEE binary16 bits)
+ *     per-head scales fp32 [num_blocks][Hkv][16]
  *     bf16 cache   [num_blocks][Hkv][16][D]      (raw bfloat16 bits)
  * Token t of sequence s lives in slot block_tables[s][t/16]*16 + t%16.
  */
@@ -168,6 +175,51 @@ void oracle_kv_write_int8(int T, int Hkv, int D, int num_blocks, const uint16_t 
   }
 }
 
+/*
+ * Per-head format: quantize one (token, head) row of n (= D) bf16 values with one fp32 scale.
+ * x = float(bf16) (exact); amax = max |x|; s = amax / 127 (correctly rounded fp32 division),
+ * stored as is; if s == 0 every code is 0, else q = clamp(rint(x / s), -127, 127), ties to
+ * even.
+ */
+void oracle_quantize_row_f32(const uint16_t *xb, int n, int8_t *codes, float *scale_out) {
+  float x[ORACLE_MAX_D];
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    x[i] = oracle_bf16_to_f32(xb[i]);
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 127.0f;
+  *scale_out = s;
+  for (int i = 0; i < n; ++i) {
+    if (s == 0.0f) {
+      codes[i] = 0;
+      continue;
+    }
+    float r = rintf(x[i] / s);
+    if (r != r) r = 0.0f;
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    codes[i] = (int8_t)r;
+  }
+}
+
+/* Quantize-on-write into the per-head format: scales fp32 [num_blocks][Hkv][16]. */
+void oracle_kv_write_int8_head(int T, int Hkv, int D, int num_blocks, const uint16_t *k, const uint16_t *v,
+                               const int32_t *slot_mapping, int8_t *k_codes, int8_t *v_codes, float *k_scales,
+                               float *v_scales) {
+  for (int t = 0; t < T; ++t) {
+    int32_t slot = slot_mapping[t];
+    if (slot < 0 || slot >= num_blocks * PAGE) continue;
+    int64_t blk = slot / PAGE, off = slot % PAGE;
+    for (int h = 0; h < Hkv; ++h) {
+      int64_t row = (blk * Hkv + h) * PAGE + off;
+      oracle_quantize_row_f32(k + ((int64_t)t * Hkv + h) * D, D, k_codes + row * D, k_scales + row);
+      oracle_quantize_row_f32(v + ((int64_t)t * Hkv + h) * D, D, v_codes + row * D, v_scales + row);
+    }
+  }
+}
+
 /* BF16 cache variant: the write is a scatter copy of the bf16 bits. */
 void oracle_kv_write_bf16(int T, int Hkv, int D, int num_blocks, const uint16_t *k, const uint16_t *v,
                           const int32_t *slot_mapping, uint16_t *k_cache, uint16_t *v_cache) {
@@ -186,11 +238,12 @@ void oracle_kv_write_bf16(int T, int Hkv, int D, int num_blocks, const uint16_t 
 /* ---------------------------------------------------------------- cache reads */
 
 typedef struct {
-  int dtype; /* 0: int8 codes + fp16 scales, 1: bf16 */
+  int dtype; /* 0: int8 codes + fp16 scales, 1: bf16, 2: int8 codes + one fp32 scale per row */
   int Hkv, D, num_blocks;
   const int8_t *k_codes, *v_codes;
   const uint16_t *k_scales, *v_scales;
   const uint16_t *k_bf16, *v_bf16;
+  const float *k_row_scales, *v_row_scales;
 } cache_view;
 
 /* Decoded K (which = 0) or V (which = 1) row of token t of sequence s, head h, in fp64.
@@ -203,6 +256,10 @@ static void read_row(const cache_view *c, const int32_t *bt_row, int t, int h, i
     const int8_t *codes = (which ? c->v_codes : c->k_codes) + row * D;
     const uint16_t *sc = (which ? c->v_scales : c->k_scales) + row * (D / GROUP);
     for (int i = 0; i < D; ++i) dst[i] = (double)codes[i] * (double)oracle_f16_to_f32(sc[i / GROUP]);
+  } else if (c->dtype == 2) {
+    const int8_t *codes = (which ? c->v_codes : c->k_codes) + row * D;
+    double sc = (double)(which ? c->v_row_scales : c->k_row_scales)[row];
+    for (int i = 0; i < D; ++i) dst[i] = (double)codes[i] * sc; /* exact: 8 + 24 significant bits */
   } else {
     const uint16_t *vals = (which ? c->v_bf16 : c->k_bf16) + row * D;
     for (int i = 0; i < D; ++i) dst[i] = (double)oracle_bf16_to_f32(vals[i]);
@@ -337,7 +394,7 @@ void oracle_decode_int8(int S, int Hq, int Hkv, int D, int num_blocks, int max_b
                         const int32_t *block_tables, const int32_t *context_lens, const int8_t *k_codes,
                         const int8_t *v_codes, const uint16_t *k_scales, const uint16_t *v_scales, const int64_t *rows,
                         int64_t n_rows, int num_splits, int max_context_len, double *out, double *lse) {
-  cache_view c = {0, Hkv, D, num_blocks, k_codes, v_codes, k_scales, v_scales, 0, 0};
+  cache_view c = {0, Hkv, D, num_blocks, k_codes, v_codes, k_scales, v_scales, 0, 0, 0, 0};
   decode_rows(&c, S, Hq, max_blocks, q, block_tables, context_lens, rows, n_rows, num_splits, max_context_len, out,
               lse);
 }
@@ -346,7 +403,16 @@ void oracle_decode_bf16(int S, int Hq, int Hkv, int D, int num_blocks, int max_b
                         const int32_t *block_tables, const int32_t *context_lens, const uint16_t *k_cache,
                         const uint16_t *v_cache, const int64_t *rows, int64_t n_rows, int num_splits,
                         int max_context_len, double *out, double *lse) {
-  cache_view c = {1, Hkv, D, num_blocks, 0, 0, 0, 0, k_cache, v_cache};
+  cache_view c = {1, Hkv, D, num_blocks, 0, 0, 0, 0, k_cache, v_cache, 0, 0};
+  decode_rows(&c, S, Hq, max_blocks, q, block_tables, context_lens, rows, n_rows, num_splits, max_context_len, out,
+              lse);
+}
+
+void oracle_decode_int8_head(int S, int Hq, int Hkv, int D, int num_blocks, int max_blocks, const uint16_t *q,
+                             const int32_t *block_tables, const int32_t *context_lens, const int8_t *k_codes,
+                             const int8_t *v_codes, const float *k_scales, const float *v_scales, const int64_t *rows,
+                             int64_t n_rows, int num_splits, int max_context_len, double *out, double *lse) {
+  cache_view c = {2, Hkv, D, num_blocks, k_codes, v_codes, 0, 0, 0, 0, k_scales, v_scales};
   decode_rows(&c, S, Hq, max_blocks, q, block_tables, context_lens, rows, n_rows, num_splits, max_context_len, out,
               lse);
 }
@@ -363,6 +429,11 @@ void oracle_f16_to_f32_array(const uint16_t *h, float *x, int64_t n) {
 /* ngroups consecutive groups of 32 bf16 values -> 32 codes and one scale each. */
 void oracle_quantize_groups(const uint16_t *x, int64_t ngroups, int8_t *codes, uint16_t *scales) {
   for (int64_t g = 0; g < ngroups; ++g) oracle_quantize_group(x + g * GROUP, GROUP, codes + g * GROUP, scales + g);
+}
+
+/* nrows consecutive rows of n bf16 values -> n codes and one fp32 scale each (per-head format). */
+void oracle_quantize_rows_f32(const uint16_t *x, int64_t nrows, int n, int8_t *codes, float *scales) {
+  for (int64_t r = 0; r < nrows; ++r) oracle_quantize_row_f32(x + r * n, n, codes + r * n, scales + r);
 }
 
 /* Thread count OpenMP will use (for reporting). */
