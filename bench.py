@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--splits", type=int, default=0, help="split count (0 = the library's choice)")
     p.add_argument("--layers", type=int, default=0, help="override the layer count (0 = the workload's)")
     p.add_argument("--no-bf16", action="store_true", help="skip the BF16-cache comparison")
+    p.add_argument("--no-head-format", action="store_true", help="skip the per-head INT8 format comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-multi-token", action="store_true", help="skip the several-query-token decode timings")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU seconds for the oracle sample")
@@ -65,8 +66,9 @@ def parse():
 
 
 def algorithmic_bytes(lens, Hkv, D, dtype):
-    """K and V bytes every step must read from HBM: codes + fp16 scales (INT8), or bf16 values."""
-    per_token_head = (2 * D + 2 * (D // 32) * 2) if dtype == "int8" else 4 * D
+    """K and V bytes every step must read from HBM: codes + fp16 scales per 32 values (INT8 q8_0),
+    codes + one fp32 scale per row (INT8 per head), or bf16 values."""
+    per_token_head = {"int8": 2 * D + 2 * (D // 32) * 2, "int8_head": 2 * D + 2 * 4, "bf16": 4 * D}[dtype]
     return int(np.sum(lens, dtype=np.int64)) * Hkv * per_token_head
 
 
@@ -461,7 +463,7 @@ def main():
     torch.cuda.set_device(0)
     cfg = W.CONFIGS[args.config]
     n_layers = args.layers or cfg.layers
-    dtypes = ["int8"] if args.no_bf16 else ["int8", "bf16"]
+    dtypes = ["int8"] + ([] if args.no_bf16 else ["bf16"]) + ([] if args.no_head_format else ["int8_head"])
     keep = 0 if args.no_cpu_baseline else n_layers
     log(f"workload {cfg.name}: {n_layers} layers, preparing caches ({', '.join(dtypes)})")
     states, host, lay = prepare(args.config, n_layers, dtypes, keep)
@@ -529,6 +531,15 @@ def main():
     if tr is not None:
         out["roofline"]["traffic"] = tr["traffic_bytes_per_launch"]
         out["roofline"]["traffic_source"] = os.path.relpath(TRAFFIC_SUMMARY, ROOT)
+    if "int8_head" in results:
+        hres = results["int8_head"]
+        out["int8_head_variant"] = {
+            "format": "int8 codes + one fp32 scale per (token, KV head): 520 B per token per head at D 256",
+            "us_per_step": round(hres["ms"] * 1e3, 1),
+            "GB_per_s": round(hres["step_bytes"] / (hres["ms"] * 1e-3) / 1e9, 1),
+            "decode_split_us": round(hres["kern_us"], 3),
+            "split_GB_per_s": round(hres["layer_bytes"] / (hres["kern_us"] * 1e-6) / 1e9, 1),
+        }
     if "bf16" in results:
         b = results["bf16"]
         out["bf16_variant"] = {

@@ -17,10 +17,11 @@ import os
 import torch
 
 __all__ = ["Cache", "KvqError", "write", "decode", "decode_mq", "choose_num_splits_mq", "decode_step", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
-           "status_string", "lib", "LIB_PATH", "INT8", "BF16"]
+           "status_string", "lib", "LIB_PATH", "INT8", "BF16", "INT8_HEAD"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
-INT8, BF16 = 0, 1
+INT8, BF16, INT8_HEAD = 0, 1, 2
+_DTYPES = {"int8": INT8, "bf16": BF16, "int8_head": INT8_HEAD}
 PAGE = 16
 
 if not os.path.exists(LIB_PATH):
@@ -97,27 +98,31 @@ def _stream(stream=None):
 class Cache:
     """One layer's paged KV cache pool in device memory (layout of include/kvq.h).
 
-    k, v: int8 [num_blocks][Hkv][16*D] (INT8) or bf16 bits as int16 [num_blocks][Hkv][16*D];
-    k_scales, v_scales: fp16 [num_blocks][Hkv][D/32][16] (INT8 only; group-major pages).
+    k, v: int8 [num_blocks][Hkv][16*D] (INT8 formats) or bf16 bits as int16 [num_blocks][Hkv][16*D];
+    k_scales, v_scales: fp16 [num_blocks][Hkv][D/32][16] ("int8": q8_0, group-major pages) or
+    fp32 [num_blocks][Hkv][16] ("int8_head": one scale per token and head).
     """
 
     def __init__(self, dtype: str, num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda"):
-        if dtype not in ("int8", "bf16"):
+        if dtype not in _DTYPES:
             raise ValueError(dtype)
         self.dtype = dtype
         self.num_blocks, self.num_kv_heads, self.head_dim = num_blocks, num_kv_heads, head_dim
         shape = (num_blocks, num_kv_heads, PAGE * head_dim)
-        if dtype == "int8":
+        if dtype in ("int8", "int8_head"):
             self.k = torch.empty(shape, dtype=torch.int8, device=device)
             self.v = torch.empty(shape, dtype=torch.int8, device=device)
-            sshape = (num_blocks, num_kv_heads, head_dim // 32, PAGE)
-            self.k_scales = torch.empty(sshape, dtype=torch.float16, device=device)
-            self.v_scales = torch.empty(sshape, dtype=torch.float16, device=device)
+            if dtype == "int8":
+                sshape, sdt = (num_blocks, num_kv_heads, head_dim // 32, PAGE), torch.float16
+            else:
+                sshape, sdt = (num_blocks, num_kv_heads, PAGE), torch.float32
+            self.k_scales = torch.empty(sshape, dtype=sdt, device=device)
+            self.v_scales = torch.empty(sshape, dtype=sdt, device=device)
         else:
             self.k = torch.empty(shape, dtype=torch.int16, device=device)
             self.v = torch.empty(shape, dtype=torch.int16, device=device)
             self.k_scales = self.v_scales = None
-        self.desc = _CacheDesc(INT8 if dtype == "int8" else BF16, num_blocks, PAGE, num_kv_heads, head_dim,
+        self.desc = _CacheDesc(_DTYPES[dtype], num_blocks, PAGE, num_kv_heads, head_dim,
                                _ptr(self.k), _ptr(self.v), _ptr(self.k_scales), _ptr(self.v_scales))
 
     def fill(self, code: int = 0x7F, scale_bits: int = 0x7BFF, bf16_bits: int = 0x7FC0):
@@ -130,6 +135,12 @@ class Cache:
             self.v.fill_(c)
             self.k_scales.view(torch.int16).fill_(s16(scale_bits))
             self.v_scales.view(torch.int16).fill_(s16(scale_bits))
+        elif self.dtype == "int8_head":  # scales: the largest finite fp32
+            c = code - 256 if code >= 128 else code
+            self.k.fill_(c)
+            self.v.fill_(c)
+            self.k_scales.fill_(torch.finfo(torch.float32).max)
+            self.v_scales.fill_(torch.finfo(torch.float32).max)
         else:
             self.k.fill_(s16(bf16_bits))
             self.v.fill_(s16(bf16_bits))

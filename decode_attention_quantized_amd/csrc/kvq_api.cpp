@@ -21,13 +21,13 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 
 int check_cache(const kvq_cache_t *c) {
   if (!c) return KVQ_ERR_INVALID_ARG;
-  if (c->dtype != KVQ_INT8_Q8_0 && c->dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (c->dtype != KVQ_INT8_Q8_0 && c->dtype != KVQ_BF16 && c->dtype != KVQ_INT8_PER_HEAD) return KVQ_ERR_UNSUPPORTED;
   if (c->block_size != kvq::kPage) return KVQ_ERR_UNSUPPORTED;
   if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
   if ((int64_t)c->num_blocks * kvq::kPage > INT32_MAX) return KVQ_ERR_INVALID_ARG;
   if (!c->k || !c->v || !aligned(c->k, 256) || !aligned(c->v, 256)) return KVQ_ERR_INVALID_ARG;
-  if (c->dtype == KVQ_INT8_Q8_0) {
+  if (c->dtype != KVQ_BF16) {
     if (!c->k_scales || !c->v_scales || !aligned(c->k_scales, 256) || !aligned(c->v_scales, 256))
       return KVQ_ERR_INVALID_ARG;
   }
@@ -113,7 +113,7 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   st = check_heads(cache, num_q_heads);
   if (st != KVQ_OK) return st;
   if (nq < 1 || nq > kMaxQueryTokens) return KVQ_ERR_INVALID_ARG;
-  if (nq > 1 && cache->dtype != KVQ_INT8_Q8_0) return KVQ_ERR_UNSUPPORTED;
+  if (nq > 1 && cache->dtype == KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
   if (num_seqs <= 0 || (need_inputs && max_blocks_per_seq <= 0)) return KVQ_ERR_INVALID_ARG;
   if (max_context_len < 1 || (need_inputs && (int64_t)max_context_len > (int64_t)max_blocks_per_seq * kvq::kPage))
     return KVQ_ERR_INVALID_ARG;
@@ -190,7 +190,9 @@ int write_impl(const kvq_cache_t *cache, const void *k, const void *v, const int
   if (num_tokens == 0) return KVQ_OK;
   if (!k || !v || !slot_mapping || !aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 4))
     return KVQ_ERR_INVALID_ARG;
-  const int per = cache->dtype == KVQ_INT8_Q8_0 ? 2 * (cache->head_dim / kvq::kGroup) : 2 * (cache->head_dim / 8);
+  const int per = cache->dtype == KVQ_INT8_Q8_0   ? 2 * (cache->head_dim / kvq::kGroup)
+                  : cache->dtype == KVQ_BF16 ? 2 * (cache->head_dim / 8)
+                                             : 2;  // per-head: one wavefront per row
   if ((int64_t)num_tokens * cache->num_kv_heads * per > (int64_t)INT32_MAX * 256) return KVQ_ERR_INVALID_ARG;
   kvq::WriteArgs a;
   a.k = static_cast<const uint16_t *>(k);
@@ -419,7 +421,8 @@ int32_t kvq_page_offset(int32_t dtype, int32_t head_dim, int32_t which, int32_t 
   if ((head_dim != 128 && head_dim != 256) || token < 0 || token >= kvq::kPage || channel < 0 ||
       channel >= head_dim || (which != 0 && which != 1))
     return -1;
-  if (dtype == KVQ_INT8_Q8_0) return (int32_t)(which ? kvq::i8_v_offset(token, channel) : kvq::i8_k_offset(token, channel));
+  if (dtype == KVQ_INT8_Q8_0 || dtype == KVQ_INT8_PER_HEAD)
+    return (int32_t)(which ? kvq::i8_v_offset(token, channel) : kvq::i8_k_offset(token, channel));
   if (dtype == KVQ_BF16)
     return (int32_t)(which ? kvq::bf16_v_offset(token, channel) : kvq::bf16_k_offset(token, channel));
   return -1;

@@ -10,14 +10,14 @@ struct WriteArgs {
   const uint16_t *k, *v;          // bf16 [T][Hkv][D]
   const int32_t *slot_mapping;    // [T]
   void *kc, *vc;                  // code / value planes
-  uint16_t *ks, *vs;              // fp16 scale planes (INT8 only)
+  uint16_t *ks, *vs;              // scale planes: fp16 (q8_0) or fp32 (per-head, as uint16_t pairs)
   int T, Hkv, D, NB;
 };
 
 struct DecodeArgs {
   const uint16_t *q;              // bf16 [S][Hq][D]
   const void *kc, *vc;            // code / value planes
-  const uint16_t *ks, *vs;        // fp16 scale planes (INT8 only)
+  const uint16_t *ks, *vs;        // scale planes: fp16 (q8_0) or fp32 (per-head); null for BF16
   const int32_t *block_tables;    // [S][max_blocks]
   const int32_t *context_lens;    // [S]
   float *o_part;                  // workspace: fp32 [S][Hq][NS][D]
@@ -32,7 +32,7 @@ struct DecodeArgs {
   int row_tiles;                  // ceil(nq * G / 16): 16-row MFMA tiles of (query token, head) pairs
 };
 
-// Each returns hipSuccess or the launch error.  dtype: 0 INT8, 1 BF16.
+// Each returns hipSuccess or the launch error.  dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head.
 hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream);
 hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream);

@@ -20,6 +20,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kvq_internal.h"
 #include "kvq_layout.h"
 
@@ -318,6 +320,78 @@ __device__ __forceinline__ void write_new_i8(const DecodeArgs &a, int64_t page, 
   }
 }
 
+// Per-head INT8 format: one fp32 scale per (token, head) row.  The row's maximum is reduced over
+// the whole wavefront; the scale is amax / 127 (fp32 division), the codes q8_code(x, scale).
+// Returns this lane's 4 codes (one byte each, channels 4 lane .. 4 lane + 3) and the scale.
+__device__ __forceinline__ uint32_t quant_row_head(uint32_t w0, uint32_t w1, float &scale) {
+  const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  scale = amax / 127.0f;
+  uint32_t codes = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) codes |= q8_code(x[i], scale) << (8 * i);
+  return codes;
+}
+
+// Stores one row's codes (K or V in-page order) and its fp32 scale; lanes with 4 lane >= D hold
+// no channel and store nothing.
+template <int D>
+__device__ __forceinline__ void store_row_head(int8_t *page_codes, float *page_scales, int which, int t, int lane,
+                                               uint32_t codes, float scale) {
+  const int c0 = 4 * lane;
+  if (c0 < D) {
+    if (which == 0) {
+      *reinterpret_cast<uint32_t *>(page_codes + i8_k_offset(t, c0)) = codes;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) page_codes[i8_v_offset(t, c0 + i)] = (int8_t)((codes >> (8 * i)) & 0xFFu);
+    }
+    if (lane == 0) page_scales[t] = scale;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void write_new_i8h(const DecodeArgs &a, int64_t page, int t, u2_t kr, u2_t vr, int lane) {
+  pin_rows(kr, vr);
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const uint32_t w0 = which ? vr[0] : kr[0], w1 = which ? vr[1] : kr[1];
+    float scale;
+    const uint32_t codes = quant_row_head(w0, w1, scale);
+    int8_t *dst = static_cast<int8_t *>(const_cast<void *>(which ? a.vc : a.kc)) + page * (kPage * D);
+    float *sc = reinterpret_cast<float *>(const_cast<uint16_t *>(which ? a.vs : a.ks)) + page * kPage;
+    store_row_head<D>(dst, sc, which, t, lane, codes, scale);
+  }
+}
+
+// Per-head INT8 format: one wavefront per (token, KV head, K or V) row; lane l quantizes
+// channels 4l .. 4l + 3 (the scale needs the whole row's maximum).
+template <int D>
+__global__ __launch_bounds__(256) void kv_write_i8h_kernel(WriteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rid >= (int64_t)a.T * a.Hkv * 2) return;
+  const int which = (int)(rid & 1);
+  const int h = (int)((rid >> 1) % a.Hkv);
+  const int t = (int)((rid >> 1) / a.Hkv);
+  const int32_t slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.NB * kPage) return;
+  const int blk = slot >> 4, off = slot & 15;
+  const uint16_t *src = (which ? a.v : a.k) + ((int64_t)t * a.Hkv + h) * D;
+  const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(src), 0, D * 2, 0x00020000);
+  const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, 0));
+  float scale;
+  const uint32_t codes = quant_row_head(w[0], w[1], scale);
+  const int64_t page = (int64_t)blk * a.Hkv + h;
+  int8_t *dst = static_cast<int8_t *>(which ? a.vc : a.kc) + page * (kPage * D);
+  float *sc = reinterpret_cast<float *>(which ? a.vs : a.ks) + page * kPage;
+  store_row_head<D>(dst, sc, which, off, lane, codes, scale);
+}
+
 // BF16 cache: a copy of the two rows into the page.
 template <int D>
 __device__ __forceinline__ void write_new_bf16(const DecodeArgs &a, int64_t page, int t, u2_t kr, u2_t vr, int lane) {
@@ -471,14 +545,15 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
 // buffer k % NBUF; the page is requested as soon as its buffer has been read out, so while the
 // wave works on one page the next NBUF - 1 are in flight.  Q and the first page are requested
 // before anything else; the other buffers fill once Q has arrived.
-template <int D, int NW, bool MQ>
+template <int D, int NW, bool MQ, int FMT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
+  constexpr bool HEADSC = FMT == 1;   // per-head format: one fp32 scale per token (else q8_0)
   constexpr int NG = D / kGroup;      // scale groups
   constexpr int NT = D / 16;          // output tiles
   constexpr int NL = D / 64;          // 16-byte code loads per lane per page
   constexpr int PAGE_B = kPage * D;   // bytes of one code page
-  constexpr int SCALE_B = kPage * NG * 2;  // bytes of one scale tile (= D)
+  constexpr int SCALE_B = HEADSC ? kPage * 4 : kPage * NG * 2;  // bytes of one scale tile
   constexpr int NBUF = kI8Buffers;
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[NW][2][SCALE_B / 4];  // K, V scale tiles (group-major)
   __shared__ __attribute__((aligned(16))) h8_t s_q[NG][64];                   // Q operand fragments
@@ -513,14 +588,22 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   // Past the end of the split the resources have size 0: the loads return zeros without
   // touching memory, so they are issued unconditionally (no divergent branch, no wait merge).
   u4_t kb[NBUF][NL], vb[NBUF][NL];
-  uint32_t ksb[NBUF], vsb[NBUF];
+  // scale registers: q8_0 one dword of the tile per lane (restaged through LDS); per-head the
+  // fp32 scales of the lane's 4 tokens
+  using scale_reg_t = typename std::conditional<HEADSC, u4_t, uint32_t>::type;
+  scale_reg_t ksb[NBUF], vsb[NBUF];
+  auto load_scales = [&](const void *plane, int64_t page, bool ok) -> scale_reg_t {
+    const auto r = page_rsrc(plane, page, SCALE_B, ok ? SCALE_B : 0);
+    if constexpr (HEADSC) return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, q4 * 16, 0, 0));
+    else return __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, 0, 0);
+  };
   auto issue_k = [&](int b, int k, int blk) {
     const bool ok = wave + k * NW < n_units;
     const int64_t page = page_of(blk);
     const auto r = page_rsrc(a.kc, page, PAGE_B, ok ? PAGE_B : 0);
 #pragma unroll
     for (int i = 0; i < NL; ++i) kb[b][i] = ld16(r, voff, 1024 * i);
-    ksb[b] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.ks, page, SCALE_B, ok ? SCALE_B : 0), lane * 4, 0, 0);
+    ksb[b] = load_scales(a.ks, page, ok);
   };
   auto issue_v = [&](int b, int k, int blk) {
     const bool ok = wave + k * NW < n_units;
@@ -528,7 +611,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     const auto r = page_rsrc(a.vc, page, PAGE_B, ok ? PAGE_B : 0);
 #pragma unroll
     for (int i = 0; i < NL; ++i) vb[b][i] = ld16(r, voff, 1024 * i);
-    vsb[b] = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(a.vs, page, SCALE_B, ok ? SCALE_B : 0), lane * 4, 0, 0);
+    vsb[b] = load_scales(a.vs, page, ok);
   };
 
   int blk[NBUF];
@@ -551,7 +634,11 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   __builtin_amdgcn_sched_barrier(0);
   const int64_t page_new = (int64_t)blk_last * a.Hkv + h;
   const int t_new = (L - 1) & (kPage - 1);
-  if (own_new && k_last == 0) write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
+  auto write_new = [&] {
+    if constexpr (HEADSC) write_new_i8h<D>(a, page_new, t_new, knew, vnew, lane);
+    else write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
+  };
+  if (own_new && k_last == 0) write_new();
   issue_k(0, 0, blk[0]);
   __builtin_amdgcn_sched_barrier(0);
   issue_v(0, 0, blk[0]);
@@ -591,7 +678,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
   const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
-  if (own_new && k_last != 0) write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
+  if (own_new && k_last != 0) write_new();
 #pragma unroll
   for (int b = 1; b < NBUF; ++b) {
     issue_k(b, b, blk[b]);
@@ -601,6 +688,9 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   int blk_next = block_of(NBUF);
 
   float m_run = -INFINITY, l_run = 0.0f;
+  // per-head format: acc holds the value sum times 2^-r_run, r_run the largest V-scale exponent
+  // seen so far (keeps P' = p * s_v * 2^-r_run in [0, 2), inside f16 range, whatever the scales)
+  int r_run = -1000;
   f4_t acc[NT];
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -613,7 +703,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   // [group][token]) holds group l / 8, tokens 2 (l % 8) and 2 (l % 8) + 1.
   const int st_dw = (((lane & 7) >> 1) * NG + (lane >> 3)) * 2 + (lane & 1);  // restaged dword of dword l
   auto stage = [&](int which, uint32_t w) {
-    if (lane < SCALE_B / 4) s_sc[wave][which][st_dw] = w;
+    if (lane < kPage * NG * 2 / 4) s_sc[wave][which][st_dw] = w;
   };
   auto scales = [&](int which, u2_t (&out)[NG]) {
     const u4_t *src = reinterpret_cast<const u4_t *>(&s_sc[wave][which][q4 * NG * 2]);
@@ -629,12 +719,29 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   auto process = [&](int b, int k) {
     const int u = wave + k * NW;  // (past the split's last page: no valid token)
     const int lim = u < n_units ? min(L - (p0 + u) * kPage, kPage) : 0;  // valid tokens of the page
+    f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (HEADSC) {
+      // ---- Q.K^T, per-head format: the groups' MFMAs accumulate in two chains, then each token's
+      // fp32 scale (tokens past the context may carry any scale: their scores are masked below)
+      f4_t c0 = {0.0f, 0.0f, 0.0f, 0.0f}, c1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const h8_t kop = i8x8_to_h8(kb[b][g >> 1][(g & 1) * 2], kb[b][g >> 1][(g & 1) * 2 + 1]);
+        if (g & 1) c1 = mfma_f16(kop, qop[g], c1);
+        else c0 = mfma_f16(kop, qop[g], c0);
+      }
+      const u4_t ks4 = ksb[b];
+      const uint32_t k0 = ks4[0], k1 = ks4[1], k2 = ks4[2], k3 = ks4[3];
+      sc[0] = (c0[0] + c1[0]) * __uint_as_float(k0);
+      sc[1] = (c0[1] + c1[1]) * __uint_as_float(k1);
+      sc[2] = (c0[2] + c1[2]) * __uint_as_float(k2);
+      sc[3] = (c0[3] + c1[3]) * __uint_as_float(k3);
+    } else {
     stage(0, ksb[b]);
     u2_t ksc[NG];
     scales(0, ksc);
     // ---- Q.K^T: one MFMA per 32-channel group, then the group's fp16 scale
     // one MFMA per group; the scale step of group g runs after group g + 1's MFMA is issued
-    f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     auto qk_group = [&](int g) -> f4_t {
       return mfma_f16(i8x8_to_h8(kb[b][g >> 1][(g & 1) * 2], kb[b][g >> 1][(g & 1) * 2 + 1]), qop[g],
                       f4_t{0.0f, 0.0f, 0.0f, 0.0f});
@@ -656,6 +763,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       __builtin_amdgcn_sched_barrier(0);
     }
     scale_group(NG - 1, c_prev);
+    }
     // ---- online softmax over the page's 16 tokens (base 2).  Padding heads (Q = 0) get finite
     // scores; their rows are never written out.
     float x[4];
@@ -684,12 +792,43 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) acc[jt] *= ar;
     }
+    const int nv = min(max(lim - 4 * q4, 0), 4);  // valid tokens among the lane's 4
+    if constexpr (HEADSC) {
+      // ---- P.V, per-head format: P' = p * s_v * 2^-r_run per token (once per page), f16 hi + lo
+      // packed along K as below.  Scales of tokens past the context are masked to 0.
+      const u4_t vs4 = vsb[b];
+      const uint32_t w0 = vs4[0], w1 = vs4[1], w2 = vs4[2], w3 = vs4[3];
+      const float sv[4] = {nv > 0 ? __uint_as_float(w0) : 0.0f, nv > 1 ? __uint_as_float(w1) : 0.0f,
+                           nv > 2 ? __uint_as_float(w2) : 0.0f, nv > 3 ? __uint_as_float(w3) : 0.0f};
+      // the page's largest V scale (the same in every lane) sets the exponent
+      const float smax = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      const int e_page = smax > 0.0f ? __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(smax)) : r_run;
+      if (e_page > r_run) {  // (uniform) exact power-of-two rescale of the accumulator
+        const float beta = ldexpf(1.0f, r_run - e_page);
+#pragma unroll
+        for (int jt = 0; jt < NT; ++jt) acc[jt] *= beta;
+        r_run = e_page;
+      }
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = p[i] * ldexpf(sv[i], -r_run);
+      const h2_t hi01 = {(_Float16)pv[0], (_Float16)pv[1]}, hi23 = {(_Float16)pv[2], (_Float16)pv[3]};
+      const h2_t lo01 = {(_Float16)(pv[0] - (float)hi01[0]), (_Float16)(pv[1] - (float)hi01[1])};
+      const h2_t lo23 = {(_Float16)(pv[2] - (float)hi23[0]), (_Float16)(pv[3] - (float)hi23[1])};
+      const h8_t pp = __builtin_bit_cast(h8_t, u4_t{__builtin_bit_cast(uint32_t, hi01), __builtin_bit_cast(uint32_t, hi23),
+                                                   __builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) {
+        uint32_t v0, v1;
+        i8x4_to_f16(vb[b][jt >> 2][jt & 3], v0, v1);
+        acc[jt] = mfma_f16(pp, __builtin_bit_cast(h8_t, u4_t{v0, v1, v0, v1}), acc[jt]);
+      }
+    } else {
     // ---- P.V: P' = p * s_v per (token, group) as f16 hi + lo, times exact f16 V codes.  V scales
     // of tokens past the context are masked to 0 (their codes and scales may be stale).
     stage(1, vsb[b]);
     u2_t vsc[NG];
     scales(1, vsc);
-    const int nv = min(max(lim - 4 * q4, 0), 4);
     const u2_t msk = {nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0xFFFFu : 0u), nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0xFFFFu : 0u)};
     // One 16x16x32 MFMA per output tile covers both parts of P': its 32 K-slots are, per lane,
     // (hi of tokens 4 q4 .. 4 q4 + 3, lo of the same tokens), and the V operand holds the lane's
@@ -720,6 +859,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each group's temporaries short-lived
     }
+    }
   };
 
   // A uniform trip count and no early exit: pages past the split's end read zeros and are
@@ -734,6 +874,11 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       __builtin_amdgcn_sched_barrier(0);
       blk_next = block_of(k + b + NBUF + 1);
     }
+  }
+  if constexpr (HEADSC) {  // back to the true value sum: acc * 2^r_run
+    const float f = ldexpf(1.0f, r_run);
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt) acc[jt] *= f;
   }
   write_partial<D, NW, MQ>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, rt);
 }
@@ -947,6 +1092,12 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
 
 hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
+  if (dtype == 2) {  // per-head INT8: one wavefront per (token, head, K or V) row, 4 rows per block
+    const unsigned grid = (unsigned)(((int64_t)a.T * a.Hkv * 2 + 3) / 4);
+    if (a.D == 256) hipLaunchKernelGGL(kv_write_i8h_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(kv_write_i8h_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const int per = (dtype == 0 ? a.D / kGroup : a.D / 8) * 2;
   const int64_t total = (int64_t)a.T * a.Hkv * per;
   const unsigned grid = (unsigned)((total + 255) / 256);
@@ -960,12 +1111,12 @@ hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int NW, bool I8>
+template <int D, int NW, bool I8, int FMT = 0>
 static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
   const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, false>), dim3(grid), dim3(NW * 64), smem, stream, a,
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, false, FMT>), dim3(grid), dim3(NW * 64), smem, stream, a,
                        a.block_tables);
   else
     hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
@@ -983,17 +1134,25 @@ static void launch_split_nw(const DecodeArgs &a, hipStream_t stream) {
 
 // Several query tokens per sequence (INT8 cache, 4 waves): one workgroup per (16-row tile, split,
 // KV head, sequence).
-template <int D>
+template <int D, int FMT>
 static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.row_tiles * a.NS);
   const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);
-  hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, true>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
+  hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, true, FMT>), dim3(grid), dim3(256), smem, stream, a,
+                     a.block_tables);
 }
 
+// dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head
 hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t stream) {
   if (dtype == 0 && a.nq > 1) {
-    if (a.D == 256) launch_split_mq<256>(a, stream);
-    else launch_split_mq<128>(a, stream);
+    if (a.D == 256) launch_split_mq<256, 0>(a, stream);
+    else launch_split_mq<128, 0>(a, stream);
+  } else if (dtype == 2 && a.nq > 1) {
+    if (a.D == 256) launch_split_mq<256, 1>(a, stream);
+    else launch_split_mq<128, 1>(a, stream);
+  } else if (dtype == 2) {
+    if (a.D == 256) launch_split<256, 4, true, 1>(a, stream);
+    else launch_split<128, 4, true, 1>(a, stream);
   } else if (dtype == 0) {
     if (a.D == 256) launch_split_nw<256, true>(a, stream);
     else launch_split_nw<128, true>(a, stream);

@@ -57,6 +57,12 @@
  *     k_scales,      binary16, [num_blocks][Hkv][D/32][16]: scale of (token t, group g = c/32)
  *     v_scales       at element ((b*Hkv + h)*(D/32) + g)*16 + t (group-major within a page, so
  *                    that the 4 scales of one group a lane needs are 8 contiguous bytes).
+ *   INT8 per head (KVQ_INT8_PER_HEAD): the half-the-memory page's description of vLLM's
+ *     int8_per_token_head cache (one shared 32-bit scale per token and head; 520 bytes per token
+ *     per head at D = 256): k, v codes exactly as for KVQ_INT8_Q8_0; k_scales, v_scales fp32
+ *     [num_blocks][Hkv][16], element (b*Hkv + h)*16 + t.  Quantizer: amax over the row's D values,
+ *     s = amax / 127 (fp32 division, stored as is), code = clamp(rint(x / s), -127, 127) with the
+ *     fp32 quotient rounded half to even, 0 when s == 0.
  *   BF16 (KVQ_BF16):  k, v bfloat16, pages of 16*D values (2*16*D bytes); element of (t, c):
  *                      K:  (((c>>5)<<6) | (((c>>3)&3)<<4) | t) << 3 | (c&7)
  *                      V:  (((c>>5)<<6) | ((t>>2)<<4) | (c&15)) << 3 | (((c>>4)&1)<<2) | (t&3)
@@ -85,8 +91,9 @@ extern "C" {
 #endif
 
 typedef enum {
-  KVQ_INT8_Q8_0 = 0, /* int8 codes + one binary16 scale per 32 values */
-  KVQ_BF16 = 1       /* bfloat16 values, no scales (comparison variant) */
+  KVQ_INT8_Q8_0 = 0,    /* int8 codes + one binary16 scale per 32 values */
+  KVQ_BF16 = 1,         /* bfloat16 values, no scales (comparison variant) */
+  KVQ_INT8_PER_HEAD = 2 /* int8 codes + one fp32 scale per (token, KV head) row (comparison format) */
 } kvq_dtype_t;
 
 typedef enum {
@@ -106,7 +113,7 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv */
   int32_t head_dim;     /* D: 128 or 256 */
   void *k, *v;          /* code / value planes (layout above) */
-  void *k_scales, *v_scales; /* binary16 scale planes (INT8), NULL for BF16 */
+  void *k_scales, *v_scales; /* scale planes: binary16 (q8_0) or fp32 (per head); NULL for BF16 */
 } kvq_cache_t;
 
 /*

@@ -44,6 +44,10 @@ class Pair:
     def gpu_logical(self):
         torch.cuda.synchronize()
         g = self.g
+        if self.dtype == "int8_head":  # codes as INT8; scales fp32 [NB][Hkv][16] (compared as bits)
+            kc = to_logical(g.k.cpu().numpy(), "int8", self.D, "k")
+            vc = to_logical(g.v.cpu().numpy(), "int8", self.D, "v")
+            return kc, vc, g.k_scales.cpu().numpy().view(np.uint32), g.v_scales.cpu().numpy().view(np.uint32)
         if self.dtype == "int8":
             kc = to_logical(g.k.cpu().numpy(), "int8", self.D, "k")
             vc = to_logical(g.v.cpu().numpy(), "int8", self.D, "v")
@@ -59,6 +63,9 @@ class Pair:
         if self.dtype == "int8":
             want = (self.o.k, self.o.v, self.o.k_scales, self.o.v_scales)
             names = ("k codes", "v codes", "k scales", "v scales")
+        elif self.dtype == "int8_head":
+            want = (self.o.k, self.o.v, self.o.k_scales.view(np.uint32), self.o.v_scales.view(np.uint32))
+            names = ("k codes", "v codes", "k scales", "v scales")
         else:
             want = (self.o.k, self.o.v)
             names = ("k", "v")
@@ -69,7 +76,12 @@ class Pair:
     def upload_oracle_cache(self):
         """Overwrite the GPU cache with the oracle's bytes (decode tests independent of kv_write)."""
         o, g = self.o, self.g
-        if self.dtype == "int8":
+        if self.dtype == "int8_head":
+            g.k.copy_(torch.from_numpy(to_physical(o.k, "int8", self.D, "k")))
+            g.v.copy_(torch.from_numpy(to_physical(o.v, "int8", self.D, "v")))
+            g.k_scales.copy_(torch.from_numpy(o.k_scales))
+            g.v_scales.copy_(torch.from_numpy(o.v_scales))
+        elif self.dtype == "int8":
             g.k.copy_(torch.from_numpy(to_physical(o.k, "int8", self.D, "k")))
             g.v.copy_(torch.from_numpy(to_physical(o.v, "int8", self.D, "v")))
             g.k_scales.view(torch.int16).copy_(torch.from_numpy(scales_to_physical(o.k_scales).view(np.int16)))
