@@ -52,6 +52,10 @@ int device_cus() {
   return cached[dev];
 }
 
+int row_tiles_for(int nq, int G) { return nq > 1 ? (nq * G + 15) / 16 : 1; }
+// Row tiles per workgroup: the waves of one workgroup share its pages across up to 4 tiles.
+int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
+
 // Split count: enough workgroups to fill every compute unit, but no split shorter than a
 // minimum number of pages, so that the merge stays small next to the stream.  A single sequence
 // runs best with one workgroup (one wave per SIMD) per compute unit and long page runs per wave.
@@ -66,8 +70,12 @@ int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus
   (void)D;
   const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
   if (max_pages <= 0) return 1;
-  const int64_t base = (int64_t)S * Hkv * row_tiles;
-  const int64_t target_wg = ((int64_t)S * row_tiles > 1 ? 2LL : 1LL) * cus;
+  // several query tokens: a workgroup holds rtw row tiles (its LDS then leaves room for one
+  // workgroup per CU), so the count is set by the workgroups per (sequence, KV head), as for one
+  // query token
+  const int rtw = rtw_for(row_tiles), groups = (row_tiles + rtw - 1) / rtw;
+  const int64_t base = (int64_t)S * Hkv * groups;
+  const int64_t target_wg = ((int64_t)S * groups > 1 ? 2LL : 1LL) * cus;
   int64_t ns = (target_wg + base - 1) / base;
   const int min_pages = 8;
   const int64_t cap = (max_pages + min_pages - 1) / min_pages;
@@ -102,7 +110,6 @@ bool bf16_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
 // unless num_splits == 0 (the heuristic reads the device's compute-unit count).
 constexpr int kMaxQueryTokens = 64;
 
-int row_tiles_for(int nq, int G) { return nq > 1 ? (nq * G + 15) / 16 : 1; }
 
 int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
                    const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
@@ -125,7 +132,8 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   const int RT = row_tiles_for(nq, num_q_heads / Hkv);
   const int NS = num_splits ? num_splits
                             : choose_splits(cache->dtype, num_seqs, Hkv, D, max_context_len, device_cus(), RT);
-  if ((int64_t)num_seqs * Hkv * NS * RT > INT32_MAX || (int64_t)num_seqs * nq * num_q_heads * (D / 64) > INT32_MAX)
+  const int RTW = rtw_for(RT), RG = (RT + RTW - 1) / RTW;
+  if ((int64_t)num_seqs * Hkv * NS * RG > INT32_MAX || (int64_t)num_seqs * nq * num_q_heads * (D / 64) > INT32_MAX)
     return KVQ_ERR_INVALID_ARG;
   // one sequence's query block and partials are addressed with 32-bit buffer offsets
   if (nq > 1 && ((int64_t)nq * num_q_heads * NS * D * 4 >= INT32_MAX || (int64_t)nq * num_q_heads * D * 2 >= INT32_MAX))
@@ -160,6 +168,8 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   a.waves = waves_for(cache->dtype, D);
   a.nq = nq;
   a.row_tiles = RT;
+  a.rtw = RTW;
+  a.row_groups = RG;
   return KVQ_OK;
 }
 

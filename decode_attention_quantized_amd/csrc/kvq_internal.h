@@ -30,6 +30,8 @@ struct DecodeArgs {
   int waves;                      // wavefronts per split workgroup (1, 2, 4 or 8)
   int nq;                         // query tokens per sequence (q [S][nq][Hq][D], causal among them)
   int row_tiles;                  // ceil(nq * G / 16): 16-row MFMA tiles of (query token, head) pairs
+  int rtw;                        // row tiles per workgroup (1, 2 or 4; its waves split into rtw groups)
+  int row_groups;                 // ceil(row_tiles / rtw): workgroups per (split, KV head, sequence)
 };
 
 // Each returns hipSuccess or the launch error.  dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head.

@@ -432,12 +432,17 @@ constexpr int merge_stride() { return (D / 16) * 256 + 32; }
 // merge; `merge` holds NW regions of merge_stride<D>() floats).  Every wave stores its
 // accumulator tiles as they sit in its registers; wave w then combines tiles w, w + NW, ...
 // of all waves for its own lanes' rows, each wave's rows weighted by 2^(m_w - M).
-template <int D, int NW, bool MQ = false>
+// Several row tiles per workgroup (RTW > 1): waves w, w + RTW, ... hold the same tile (rl = w % RTW)
+// for different pages and merge among themselves.
+template <int D, int NW, bool MQ = false, int RTW = 1>
 __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h, int j, int wave, int n16, int q4,
                                               float m_run, float l_run, const f4_t (&acc)[D / 16], float *merge,
                                               int rt = 0) {
   constexpr int NT = D / 16;
   constexpr int ST = merge_stride<D>();
+  constexpr int NWP = NW / RTW;  // waves per row tile
+  static_assert(NW % RTW == 0 && NT % NWP == 0, "waves must split evenly over row tiles and output tiles");
+  const int rl = wave % RTW, pw = wave / RTW;
   const int G = a.G;
   const int lane = q4 * 16 + n16;
   l_run = rows_sum(l_run);
@@ -467,18 +472,18 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
     // Every lane computes; lanes of padding heads (4 q4 + i >= G) read unused LDS and their stores
     // fall past the end of the resources below (rows of heads 0 .. G-1 only), so no branches.
     // weights of every wave for this lane's rows (heads 4 q4 .. 4 q4 + 3)
-    f4_t mw[NW], wt[NW];
+    f4_t mw[NWP], wt[NWP];
     f4_t M = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      mw[w] = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 4 * q4);
+    for (int w = 0; w < NWP; ++w) {
+      mw[w] = *reinterpret_cast<const f4_t *>(merge + (rl + w * RTW) * ST + NT * 256 + 4 * q4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) M[i] = fmaxf(M[i], mw[w][i]);
     }
     f4_t Lsum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const f4_t lw = *reinterpret_cast<const f4_t *>(merge + w * ST + NT * 256 + 16 + 4 * q4);
+    for (int w = 0; w < NWP; ++w) {
+      const f4_t lw = *reinterpret_cast<const f4_t *>(merge + (rl + w * RTW) * ST + NT * 256 + 16 + 4 * q4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         wt[w][i] = (mw[w][i] == -INFINITY) ? 0.0f : exp2_w(mw[w][i] - M[i]);  // waves without pages: 0
@@ -510,7 +515,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
 #pragma unroll
       for (int i = 0; i < 4; ++i) row_off[i] = (4 * q4 + i) * a.NS;
     }
-    if (wave == 0 && n16 == 0) {
+    if (pw == 0 && n16 == 0) {
       const auto rml = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2 *>(ml_base), 0, rows_valid * 8, 0x00020000);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -518,36 +523,41 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
             __builtin_bit_cast(u2_t, make_float2(M[i], Lsum[i])), rml, row_off[i] * 8, 0, 0);
     }
     const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o_base), 0, rows_valid * D * 4, 0x00020000);
-    f4_t o[NT / NW];
+    f4_t o[NT / NWP];
 #pragma unroll
-    for (int t = 0; t < NT / NW; ++t) {  // every LDS read is issued before the first store
-      const int jt = wave + t * NW;
+    for (int t = 0; t < NT / NWP; ++t) {  // every LDS read is issued before the first store
+      const int jt = pw + t * NWP;
       o[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const f4_t v = *reinterpret_cast<const f4_t *>(merge + w * ST + (jt * 64 + lane) * 4);
+      for (int w = 0; w < NWP; ++w) {
+        const f4_t v = *reinterpret_cast<const f4_t *>(merge + (rl + w * RTW) * ST + (jt * 64 + lane) * 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[t][i] = fmaf(wt[w][i], v[i], o[t][i]);
       }
     }
 #pragma unroll
-    for (int t = 0; t < NT / NW; ++t)
+    for (int t = 0; t < NT / NWP; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[t][i]), ro,
-                                              (row_off[i] * D + 16 * (wave + t * NW) + n16) * 4, 0, 0);
+                                              (row_off[i] * D + 16 * (pw + t * NWP) + n16) * 4, 0, 0);
   }
 }
 
 // ---- INT8 cache: 1-page units in a ring of register buffers, f16 MFMA for both products
 //
-// A wave owns pages p0 + wave + k * NW (k = 0, 1, ...) of its split.  Page k lands in register
+// A wave owns pages p0 + wave + k * NW (k = 0, 1, ...) of its split (several query tokens with
+// RTW row tiles per workgroup: pages p0 + wave / RTW + k * NW / RTW, for tile wave % RTW).  Page k lands in register
 // buffer k % NBUF; the page is requested as soon as its buffer has been read out, so while the
 // wave works on one page the next NBUF - 1 are in flight.  Q and the first page are requested
 // before anything else; the other buffers fill once Q has arrived.
-template <int D, int NW, bool MQ, int FMT>
+template <int D, int NW, int MQR, int FMT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
+  constexpr bool MQ = MQR > 0;        // several query tokens: rows are (query token, head) pairs
+  constexpr int RTW = MQ ? MQR : 1;   // row tiles per workgroup (MQ)
+  constexpr int NWP = NW / RTW;       // waves that split the pages of one row tile
+  static_assert(NW % RTW == 0, "row tiles must split the waves evenly");
   constexpr bool HEADSC = FMT == 1;   // per-head format: one fp32 scale per token (else q8_0)
   constexpr int NG = D / kGroup;      // scale groups
   constexpr int NT = D / 16;          // output tiles
@@ -556,19 +566,22 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   constexpr int SCALE_B = HEADSC ? kPage * 4 : kPage * NG * 2;  // bytes of one scale tile
   constexpr int NBUF = kI8Buffers;
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[NW][2][SCALE_B / 4];  // K, V scale tiles (group-major)
-  __shared__ __attribute__((aligned(16))) h8_t s_q[NG][64];                   // Q operand fragments
+  __shared__ __attribute__((aligned(16))) h8_t s_q[RTW][NG][64];              // Q operand fragments per row tile
   __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];              // rescale factors, per head
   extern __shared__ float s_merge[];                                          // [NW][G*D + 32] (dynamic)
 
   const int32_t *__restrict__ context_lens = a.context_lens;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
+  const int rl = wave % RTW, pw = wave / RTW;  // row tile within the workgroup, page-wave index
   const int n16 = lane & 15, q4 = lane >> 4;
   const int j = blockIdx.x % a.NS;
-  // (MQ: the workgroup's 16-row tile of (query token, head) pairs, between split and KV head)
-  const int rt = MQ ? (blockIdx.x / a.NS) % a.row_tiles : 0;
-  const int h = (blockIdx.x / (a.NS * (MQ ? a.row_tiles : 1))) % a.Hkv;
-  const int s = blockIdx.x / (a.NS * (MQ ? a.row_tiles : 1) * a.Hkv);
+  // (MQ: the workgroup's group of RTW 16-row tiles of (query token, head) pairs, between split and
+  // KV head; this wave's tile is rt)
+  const int rg = MQ ? (blockIdx.x / a.NS) % a.row_groups : 0;
+  const int rt = rg * RTW + rl;
+  const int h = (blockIdx.x / (a.NS * (MQ ? a.row_groups : 1))) % a.Hkv;
+  const int s = blockIdx.x / (a.NS * (MQ ? a.row_groups : 1) * a.Hkv);
   const int L = max(0, min(context_lens[s], a.max_context_len));
   const int P = (L + kPage - 1) / kPage;
   const int p0 = j * a.cpp;
@@ -581,7 +594,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
 
   // Block id of page k of the wave: a scalar load (the block table is only read here), issued
   // one page ahead of its use so that its latency hides behind a page's work.
-  auto block_of = [&](int k) -> int { return btrow[min(p0 + wave + k * NW, p1 - 1)]; };
+  auto block_of = [&](int k) -> int { return btrow[min(p0 + pw + k * NWP, p1 - 1)]; };
   auto page_of = [&](int blk) -> int64_t { return (int64_t)min(max(blk, 0), a.NB - 1) * a.Hkv + h; };
 
   // ---- register buffers: K / V codes and the page's K / V scale tiles (one dword per lane).
@@ -598,7 +611,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     else return __builtin_amdgcn_raw_buffer_load_b32(r, lane * 4, 0, 0);
   };
   auto issue_k = [&](int b, int k, int blk) {
-    const bool ok = wave + k * NW < n_units;
+    const bool ok = pw + k * NWP < n_units;
     const int64_t page = page_of(blk);
     const auto r = page_rsrc(a.kc, page, PAGE_B, ok ? PAGE_B : 0);
 #pragma unroll
@@ -606,7 +619,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     ksb[b] = load_scales(a.ks, page, ok);
   };
   auto issue_v = [&](int b, int k, int blk) {
-    const bool ok = wave + k * NW < n_units;
+    const bool ok = pw + k * NWP < n_units;
     const int64_t page = page_of(blk);
     const auto r = page_rsrc(a.vc, page, PAGE_B, ok ? PAGE_B : 0);
 #pragma unroll
@@ -622,7 +635,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   const int blk_last = btrow[P - 1];
   const bool own_new =
       !MQ && a.k_new != nullptr && p1 == P && wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
-  const int k_last = (n_units - 1) / NW;
+  const int k_last = (n_units - 1) / NWP;
   // MQ: the lane's row sees keys 0 .. L - nq + token (causal among the query tokens)
   int L_row = L;
   if constexpr (MQ) L_row = L - a.nq + (16 * rt + n16) / a.G + 1;
@@ -660,7 +673,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       frexpf(qmax, &e2);
       shift = 15 - e2;
     }
-    if (wave == 0) {
+    if (pw == 0) {  // (one wave per row tile)
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         h8_t qg;
@@ -669,7 +682,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
           qg[2 * e] = (_Float16)ldexpf(bf16_lo(qraw[g][e]), shift);
           qg[2 * e + 1] = (_Float16)ldexpf(bf16_hi(qraw[g][e]), shift);
         }
-        s_q[g][lane] = qg;
+        s_q[rl][g][lane] = qg;
       }
     }
     // LDS-only fences: __syncthreads would also wait for the page loads in flight
@@ -697,7 +710,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   // the Q operand stays in registers for the whole split
   h8_t qop[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) qop[g] = s_q[g][lane];
+  for (int g = 0; g < NG; ++g) qop[g] = s_q[rl][g][lane];
   // Scale tiles are restaged token-quad-major ([q4][group][4 tokens]) so that a lane reads the
   // scales of its 4 tokens for all groups with 8*NG contiguous bytes.  Tile dword l (group-major
   // [group][token]) holds group l / 8, tokens 2 (l % 8) and 2 (l % 8) + 1.
@@ -717,7 +730,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
 
   // One page from buffer b: Q.K^T, one online-softmax update, P.V.
   auto process = [&](int b, int k) {
-    const int u = wave + k * NW;  // (past the split's last page: no valid token)
+    const int u = pw + k * NWP;  // (past the split's last page: no valid token)
     const int lim = u < n_units ? min(L - (p0 + u) * kPage, kPage) : 0;  // valid tokens of the page
     f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (HEADSC) {
@@ -864,7 +877,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
 
   // A uniform trip count and no early exit: pages past the split's end read zeros and are
   // fully masked (p = 0), which keeps the in-flight buffers in fixed registers across the loop.
-  const int my_units = wave < n_units ? (n_units - wave + NW - 1) / NW : 0;
+  const int my_units = pw < n_units ? (n_units - pw + NWP - 1) / NWP : 0;
   for (int k = 0; k < my_units; k += NBUF) {
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
@@ -880,7 +893,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) acc[jt] *= f;
   }
-  write_partial<D, NW, MQ>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, rt);
+  write_partial<D, NW, MQ, RTW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, rt);
 }
 
 // ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
@@ -1116,7 +1129,7 @@ static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
   const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, false, FMT>), dim3(grid), dim3(NW * 64), smem, stream, a,
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, 0, FMT>), dim3(grid), dim3(NW * 64), smem, stream, a,
                        a.block_tables);
   else
     hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
@@ -1136,10 +1149,14 @@ static void launch_split_nw(const DecodeArgs &a, hipStream_t stream) {
 // KV head, sequence).
 template <int D, int FMT>
 static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
-  const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.row_tiles * a.NS);
+  const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.row_groups * a.NS);
   const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);
-  hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, true, FMT>), dim3(grid), dim3(256), smem, stream, a,
-                     a.block_tables);
+  if (a.rtw == 4)
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
+  else if (a.rtw == 2)
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
+  else
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 1, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
 }
 
 // dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head

@@ -179,9 +179,9 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
  *                bytes, where splits is num_splits or, for 0, kvq_choose_num_splits_mq(...).
  *   other arguments as kvq_decode_attention.  A query token with no visible key (L < n_q) gets
  *   out = 0 and lse = -inf.  Returns KVQ_ERR_UNSUPPORTED for a BF16 cache with n_q > 1.
- * The (query token, head) pairs of one KV head form the rows of the MFMA tiles: n_q * G <= 16
- * costs the same cache reads as one query token; beyond that each further 16 rows read the
- * sequence's pages again.
+ * The (query token, head) pairs of one KV head form the rows of 16-row MFMA tiles; up to 4
+ * tiles (n_q * G <= 64) share one workgroup and one read of each page, each further 4 tiles
+ * read the sequence's pages again.
  */
 int kvq_decode_attention_mq(const kvq_cache_t *cache, const void *q, int32_t num_query_tokens,
                             const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
