@@ -212,6 +212,43 @@ def decode(cache: OracleCache, q_bf16: np.ndarray, block_tables: np.ndarray, con
     return out, lse
 
 
+def quantized_q(q_bf16: np.ndarray) -> np.ndarray:
+    """Integer Q.K (opt-in): Q [..., D] quantized with the cache's own q8_0 rule (one fp16 scale per
+    32 values, codes against the stored scale) and decoded, code * scale, as fp64."""
+    q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+    D = q.shape[-1]
+    codes, scales = quantize_groups(q.reshape(-1, GROUP))
+    qd = codes.astype(np.float64) * f16_to_f32(scales).astype(np.float64)[:, None]
+    return qd.reshape(q.shape[:-1] + (D,))
+
+
+def decode_int8_qk(cache: OracleCache, q_bf16: np.ndarray, block_tables: np.ndarray, context_lens: np.ndarray):
+    """Decode attention with integer Q.K (the long-context page's integer dot-product option:
+    Q quantized per 32 values like the cache): the plain definition softmax(q^ K^T / sqrt(D)) V in
+    fp64 over the decoded cache, with q^ = quantized_q(q).  Returns (out [S][Hq][D], lse [S][Hq])."""
+    qd = quantized_q(q_bf16)
+    S, Hq, D = qd.shape
+    K = dequantized_rows(cache, "k")
+    V = dequantized_rows(cache, "v")
+    G = Hq // cache.num_kv_heads
+    out = np.zeros((S, Hq, D))
+    lse = np.full((S, Hq), -np.inf)
+    bt = np.asarray(block_tables)
+    for s_ in range(S):
+        L = int(context_lens[s_])
+        if L <= 0:
+            continue
+        t = np.arange(L)
+        blk, off = bt[s_, t // PAGE], t % PAGE
+        for hq in range(Hq):
+            z = K[blk, hq // G, off] @ qd[s_, hq] / np.sqrt(D)
+            m = z.max()
+            w = np.exp(z - m)
+            out[s_, hq] = (w @ V[blk, hq // G, off]) / w.sum()
+            lse[s_, hq] = m + np.log(w.sum())
+    return out, lse
+
+
 def decode_mq(cache: OracleCache, q_bf16: np.ndarray, block_tables: np.ndarray, context_lens: np.ndarray):
     """Decode attention for n_q query tokens per sequence, causal among them, in fp64.
 

@@ -328,3 +328,44 @@ def test_multi_token_more_queries_than_context():
     assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
     ref, rlse = _bruteforce_mq(cache, q, bt, lens)
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ integer Q.K (opt-in)
+
+def test_quantized_q_error_bound_and_on_grid():
+    rng = np.random.default_rng(31)
+    q = f32_to_bf16_bits((rng.standard_normal((3, 6, 64)) * np.exp2(rng.uniform(-6, 6, (3, 6, 1)))).astype(np.float32))
+    qd = O.quantized_q(q)
+    x = bf16_bits_to_f32(q).astype(np.float64).reshape(-1, 32)
+    amax = np.abs(x).max(axis=1, keepdims=True)
+    # half a scale step, the scale being within half an fp16 ulp of amax/127
+    assert np.all(np.abs(x - qd.reshape(-1, 32)) <= amax / 127 * (0.5 + 2.0 ** -10) + 1e-300)
+    # values on the q8_0 grid are reproduced exactly
+    ints = rng.integers(-127, 128, size=(2, 4, 64))
+    ints[..., ::32] = 127
+    qg = f32_to_bf16_bits((ints * 2.0 ** -3).astype(np.float32))
+    assert np.array_equal(O.quantized_q(qg), ints * 2.0 ** -3)
+
+
+@pytest.mark.parametrize("dtype", ["int8", "bf16"])
+def test_integer_qk_equals_decode_on_grid_queries(dtype):
+    """With queries already on the q8_0 grid, quantizing Q changes nothing: the integer-Q.K
+    definition must equal the (independently pinned) decode."""
+    cache, _, bt, lens = _problem(32, [70, 16, 1], 8, 2, 128, dtype)
+    rng = np.random.default_rng(33)
+    ints = rng.integers(-127, 128, size=(3, 8, 128))
+    ints[..., ::32] = 127
+    q = f32_to_bf16_bits((ints * 2.0 ** -5).astype(np.float32))
+    out, lse = O.decode_int8_qk(cache, q, bt, lens)
+    ref, rlse = O.decode(cache, q, bt, lens)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12) and np.allclose(lse, rlse, rtol=1e-12, atol=1e-12)
+
+
+def test_integer_qk_error_is_the_query_rounding():
+    """On random queries the integer-Q.K result differs from decode with the exact query, by a
+    small amount set by the query's rounding (the pages report about 1-2%)."""
+    cache, q, bt, lens = _problem(34, [200, 33], 6, 2, 64, "int8")
+    out, lse = O.decode_int8_qk(cache, q, bt, lens)
+    ref, _ = O.decode(cache, q, bt, lens)
+    d = np.abs(out - ref)
+    assert 0 < d.max() < 0.1
