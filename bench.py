@@ -53,6 +53,7 @@ def parse():
     p.add_argument("--no-head-format", action="store_true", help="skip the per-head INT8 format comparison")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-multi-token", action="store_true", help="skip the several-query-token decode timings")
+    p.add_argument("--no-int-qk", action="store_true", help="skip the integer Q.K timing")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU seconds for the oracle sample")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     p.add_argument("--sweep", action="store_true",
@@ -155,6 +156,21 @@ def time_step(torch, step, steps, warmup, eager):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     return e0.elapsed_time(e1) / steps, wall
+
+
+def time_int_qk(torch, K, layers, S, Hq, mcl, ns, n_layers, steps, warmup):
+    """us per step of attention alone (split + merge for every layer, no cache write) with the
+    exact f16 Q.K and with integer Q.K, at the same split count; graph replay."""
+    res = {}
+    ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
+    for name, iq in (("f16_qk", False), ("int8_qk", True)):
+        def step():
+            for L in layers:
+                K.decode(L.cache, L.q, L.bt, L.lens, mcl, ns, out=L.out, lse=L.lse, workspace=ws, int_qk=iq)
+        ms, _ = time_step(torch, step, steps, warmup, False)
+        res[name + "_us_per_step"] = round(ms * 1e3, 1)
+        log(f"attention only ({name}): {ms * 1e3:.1f} us/step")
+    return res
 
 
 def time_multi_token(torch, K, layers, S, Hq, D, mcl, lens, Hkv, n_layers, steps, warmup):
@@ -549,6 +565,9 @@ def main():
             "decode_split_us": round(b["kern_us"], 3),
             "int8_speedup_step": round(b["ms"] / r["ms"], 3),
         }
+    if not args.no_int_qk:
+        out["int8_qk_variant"] = time_int_qk(torch, K, states["int8"], S, Hq, mcl, r["ns"], n_layers,
+                                             args.steps, args.warmup)
     if not args.no_multi_token:
         out["multi_token"] = time_multi_token(torch, K, states["int8"], S, Hq, D, mcl, lens, Hkv, n_layers,
                                               args.steps, args.warmup)

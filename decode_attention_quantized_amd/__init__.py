@@ -50,6 +50,8 @@ lib.kvq_choose_num_splits.restype = _i32
 _DEC = [_CP, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kvq_decode_attention.argtypes = _DEC
 lib.kvq_decode_attention.restype = ctypes.c_int
+lib.kvq_decode_attention_int8qk.argtypes = _DEC
+lib.kvq_decode_attention_int8qk.restype = ctypes.c_int
 lib.kvq_check_decode.argtypes = _DEC
 lib.kvq_check_decode.restype = ctypes.c_int
 _STEP = [_CP, _P, _P] + _DEC[1:]
@@ -207,11 +209,15 @@ def _decode_args(cache, q, block_tables, context_lens, max_context_len, num_spli
 
 
 def decode(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int = 0, *,
-           out=None, lse=None, workspace=None, want_lse: bool = True, checked: bool = False, stream=None):
-    """Split-KV decode attention; returns (out fp32 [S][Hq][D], lse fp32 [S][Hq] or None)."""
+           out=None, lse=None, workspace=None, want_lse: bool = True, checked: bool = False, int_qk: bool = False,
+           stream=None):
+    """Split-KV decode attention; returns (out fp32 [S][Hq][D], lse fp32 [S][Hq] or None).
+    int_qk: integer Q.K (Q quantized like the cache; q8_0 cache only; not with checked)."""
+    if int_qk and checked:
+        raise ValueError("integer Q.K has no checked mode")
     args, out, lse = _decode_args(cache, q, block_tables, context_lens, max_context_len, num_splits, out, lse,
                                   workspace, want_lse)
-    fn = lib.kvq_check_decode if checked else lib.kvq_decode_attention
+    fn = lib.kvq_check_decode if checked else (lib.kvq_decode_attention_int8qk if int_qk else lib.kvq_decode_attention)
     _check(fn(ctypes.byref(cache.desc), *args, _stream(stream)), "kvq_decode_attention")
     return out, lse
 

@@ -167,6 +167,7 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   a.D = D;
   a.waves = waves_for(cache->dtype, D);
   a.nq = nq;
+  a.int_qk = 0;
   a.row_tiles = RT;
   a.rtw = RTW;
   a.row_groups = RG;
@@ -319,6 +320,22 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          void *workspace, size_t workspace_bytes_given, void *stream) {
   return decode_impl(cache, nullptr, nullptr, q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
                      num_seqs, num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
+}
+
+int kvq_decode_attention_int8qk(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                                int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
+                                void *workspace, size_t workspace_bytes_given, void *stream) {
+  kvq::DecodeArgs a;
+  int st = prepare_decode(cache, q, block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                          num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, true, true, a);
+  if (st != KVQ_OK) return st;
+  if (cache->dtype != KVQ_INT8_Q8_0) return KVQ_ERR_UNSUPPORTED;
+  a.int_qk = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kvq::launch_decode_split(cache->dtype, a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
+  if (kvq::launch_decode_merge(a, s) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
+  return KVQ_OK;
 }
 
 int kvq_decode_attention_mq(const kvq_cache_t *cache, const void *q, int32_t num_query_tokens,

@@ -33,6 +33,7 @@ typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -559,6 +560,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   constexpr int NWP = NW / RTW;       // waves that split the pages of one row tile
   static_assert(NW % RTW == 0, "row tiles must split the waves evenly");
   constexpr bool HEADSC = FMT == 1;   // per-head format: one fp32 scale per token (else q8_0)
+  constexpr bool IQK = FMT == 2;      // q8_0 with integer Q.K: Q quantized per 32 values like the cache
   constexpr int NG = D / kGroup;      // scale groups
   constexpr int NT = D / 16;          // output tiles
   constexpr int NL = D / 64;          // 16-byte code loads per lane per page
@@ -690,7 +692,36 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
-  const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
+  const float cmul = ldexpf(kLog2e / sqrtf((float)D), IQK ? 0 : -shift);
+  // integer Q.K: every wave quantizes its Q rows with the cache's q8_0 rule (fp16 scale of the
+  // group's amax / 127, codes against the stored scale): qi[g] holds the lane's 8 codes of group g
+  // (the B operand of v_mfma_i32_16x16x32_i8), sq[g] the row's scale for group g
+  uint64_t qi[IQK ? NG : 1];
+  float sq[IQK ? NG : 1];
+  if constexpr (IQK) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_lo(qraw[g][e]);
+        x[2 * e + 1] = bf16_hi(qraw[g][e]);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+      amax = rows_max(amax);  // the group's 32 values sit in the 4 lanes of the row
+      const float sc16 = (float)q8_scale(amax);
+      uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo |= q8_code(x[e], sc16) << (8 * e);
+        hi |= q8_code(x[4 + e], sc16) << (8 * e);
+      }
+      qi[g] = ((uint64_t)hi << 32) | lo;
+      sq[g] = sc16;
+    }
+  }
   if (own_new && k_last != 0) write_new();
 #pragma unroll
   for (int b = 1; b < NBUF; ++b) {
@@ -756,8 +787,15 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     // ---- Q.K^T: one MFMA per 32-channel group, then the group's fp16 scale
     // one MFMA per group; the scale step of group g runs after group g + 1's MFMA is issued
     auto qk_group = [&](int g) -> f4_t {
-      return mfma_f16(i8x8_to_h8(kb[b][g >> 1][(g & 1) * 2], kb[b][g >> 1][(g & 1) * 2 + 1]), qop[g],
-                      f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      if constexpr (IQK) {  // exact int32 dot products of the codes, as fp32 times the Q scale
+        const uint32_t d0 = kb[b][g >> 1][(g & 1) * 2], d1 = kb[b][g >> 1][(g & 1) * 2 + 1];
+        const auto ci = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)(((uint64_t)d1 << 32) | d0), (long)qi[g],
+                                                              v4i_t{0, 0, 0, 0}, 0, 0, 0);
+        return f4_t{(float)ci[0] * sq[g], (float)ci[1] * sq[g], (float)ci[2] * sq[g], (float)ci[3] * sq[g]};
+      } else {
+        return mfma_f16(i8x8_to_h8(kb[b][g >> 1][(g & 1) * 2], kb[b][g >> 1][(g & 1) * 2 + 1]), qop[g],
+                        f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      }
     };
     auto scale_group = [&](int g, const f4_t &c) {
       const u2_t sw = ksc[g];
@@ -1170,6 +1208,9 @@ hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t strea
   } else if (dtype == 2) {
     if (a.D == 256) launch_split<256, 4, true, 1>(a, stream);
     else launch_split<128, 4, true, 1>(a, stream);
+  } else if (dtype == 0 && a.int_qk) {
+    if (a.D == 256) launch_split<256, 4, true, 2>(a, stream);
+    else launch_split<128, 4, true, 2>(a, stream);
   } else if (dtype == 0) {
     if (a.D == 256) launch_split_nw<256, true>(a, stream);
     else launch_split_nw<128, true>(a, stream);

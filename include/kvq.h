@@ -188,6 +188,21 @@ int kvq_decode_attention_mq(const kvq_cache_t *cache, const void *q, int32_t num
                             int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
                             float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * kvq_decode_attention with integer Q.K (opt-in; INT8 q8_0 cache only, else KVQ_ERR_UNSUPPORTED).
+ * Half-the-memory page, section "Read the compressed cache without copying it first": Q is
+ * quantized to int8 once, like the cache (one fp16 scale per 32 values, codes against the stored
+ * scale), and Q.K runs as integer dot products on the int8 keys (v_mfma_i32_16x16x32_i8), each
+ * 32-channel group's exact int32 sum scaled by its Q and K scales.  The result is attention with
+ * the quantized query: it differs from kvq_decode_attention by the query's rounding (about 1% on
+ * the workloads, as the page reports for its card); off by default for that reason.  Same arguments
+ * and workspace as kvq_decode_attention.
+ */
+int kvq_decode_attention_int8qk(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
+                                int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 /* Split count kvq_decode_attention_mq uses for num_splits == 0 (negative status on error). */
 int32_t kvq_choose_num_splits_mq(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_query_tokens,
                                  int32_t num_q_heads, int32_t max_context_len);
