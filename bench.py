@@ -193,6 +193,22 @@ def time_multi_token(torch, K, layers, S, Hq, D, mcl, lens, Hkv, n_layers, steps
         res[str(nq)] = {"us_per_step": round(ms * 1e3, 1), "num_splits": ns,
                         "GB_per_s": round(algorithmic_bytes(lens, Hkv, D, "int8") * n_layers / (ms * 1e-3) / 1e9, 1)}
         log(f"int8 decode with {nq} query tokens: {ms * 1e3:.1f} us/step, splits {ns}")
+    # a prompt section: the last 2048 positions of the context attend over the cache, causally among
+    # themselves (one layer; flops 4 * Hq * D * sum of the visible keys of every query)
+    nq, L = 2048, int(mcl)
+    q = torch.randn((S, nq, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    ns = K.choose_num_splits_mq(layers[0].cache, S, nq, Hq, mcl)
+    ws = torch.empty(K.workspace_bytes(layers[0].cache, S * nq, Hq, ns), dtype=torch.uint8, device="cuda")
+    o = torch.empty((S, nq, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((S, nq, Hq), dtype=torch.float32, device="cuda")
+
+    def section():
+        K.decode_mq(layers[0].cache, q, layers[0].bt, layers[0].lens, mcl, ns, out=o, lse=lse, workspace=ws)
+    ms, _ = time_step(torch, section, max(steps // 10, 3), 1, False)
+    flops = 4.0 * Hq * D * S * sum(L - nq + i + 1 for i in range(nq))
+    res["prompt_section_2048"] = {"us_per_layer": round(ms * 1e3, 1), "num_splits": ns,
+                                  "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1)}
+    log(f"prompt section of {nq} tokens: {ms * 1e3:.1f} us per layer, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
     return res
 
 

@@ -52,7 +52,12 @@ int device_cus() {
   return cached[dev];
 }
 
-int row_tiles_for(int nq, int G) { return nq > 1 ? (nq * G + 15) / 16 : 1; }
+// Several query tokens: a workgroup holds up to 64 (query token, head) rows, 4 tiles of 16; longer
+// runs of query tokens (a prefill chunk) are cut into chunks of qchunk tokens, each attending over
+// the keys up to its own last token.
+int qchunk_for(int nq, int G) { return nq <= 64 / G ? nq : 64 / G; }
+int chunks_for(int nq, int G) { return (nq + qchunk_for(nq, G) - 1) / qchunk_for(nq, G); }
+int row_tiles_for(int nq, int G) { return nq > 1 ? (qchunk_for(nq, G) * G + 15) / 16 : 1; }
 // Row tiles per workgroup: the waves of one workgroup share its pages across up to 4 tiles.
 int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 
@@ -65,7 +70,8 @@ int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 // 4K and 32K tokens, 4 sequences of 2K-32K, 32 sequences of 512-8K).
 // (row_tiles > 1: several query tokens per sequence, one workgroup per 16-row tile of (query
 // token, head) pairs; the tiles of one split count as a batch.)
-int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus, int row_tiles = 1) {
+int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus, int row_tiles = 1,
+                  int chunks = 1) {
   (void)dtype;
   (void)D;
   const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
@@ -73,7 +79,7 @@ int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus
   // several query tokens: a workgroup holds rtw row tiles (its LDS then leaves room for one
   // workgroup per CU), so the count is set by the workgroups per (sequence, KV head), as for one
   // query token
-  const int rtw = rtw_for(row_tiles), groups = (row_tiles + rtw - 1) / rtw;
+  const int rtw = rtw_for(row_tiles), groups = (row_tiles + rtw - 1) / rtw * chunks;
   const int64_t base = (int64_t)S * Hkv * groups;
   const int64_t target_wg = ((int64_t)S * groups > 1 ? 2LL : 1LL) * cus;
   int64_t ns = (target_wg + base - 1) / base;
@@ -108,7 +114,7 @@ bool bf16_finite(uint16_t b) { return (b & 0x7F80u) != 0x7F80u; }
 
 // Validates the decode arguments and fills the kernel argument block; no HIP call is made
 // unless num_splits == 0 (the heuristic reads the device's compute-unit count).
-constexpr int kMaxQueryTokens = 64;
+constexpr int kMaxQueryTokens = 65536;
 
 
 int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block_tables, int32_t max_blocks_per_seq,
@@ -129,11 +135,13 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   if (need_inputs && (!q || !block_tables || !aligned(q, 16) || !aligned(block_tables, 4))) return KVQ_ERR_INVALID_ARG;
   if (need_outputs && (!out || !aligned(out, 16) || (lse && !aligned(lse, 4)))) return KVQ_ERR_INVALID_ARG;
   const int D = cache->head_dim, Hkv = cache->num_kv_heads;
-  const int RT = row_tiles_for(nq, num_q_heads / Hkv);
+  const int Gq = num_q_heads / Hkv;
+  const int RT = row_tiles_for(nq, Gq), CH = chunks_for(nq, Gq);
   const int NS = num_splits ? num_splits
-                            : choose_splits(cache->dtype, num_seqs, Hkv, D, max_context_len, device_cus(), RT);
+                            : choose_splits(cache->dtype, num_seqs, Hkv, D, max_context_len, device_cus(), RT, CH);
   const int RTW = rtw_for(RT), RG = (RT + RTW - 1) / RTW;
-  if ((int64_t)num_seqs * Hkv * NS * RG > INT32_MAX || (int64_t)num_seqs * nq * num_q_heads * (D / 64) > INT32_MAX)
+  if ((int64_t)num_seqs * CH * Hkv * NS * RG > INT32_MAX ||
+      (int64_t)num_seqs * nq * num_q_heads * (D / 64) > INT32_MAX)
     return KVQ_ERR_INVALID_ARG;
   // one sequence's query block and partials are addressed with 32-bit buffer offsets
   if (nq > 1 && ((int64_t)nq * num_q_heads * NS * D * 4 >= INT32_MAX || (int64_t)nq * num_q_heads * D * 2 >= INT32_MAX))
@@ -167,6 +175,8 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   a.D = D;
   a.waves = waves_for(cache->dtype, D);
   a.nq = nq;
+  a.qchunk = qchunk_for(nq, Gq);
+  a.chunks = CH;
   a.int_qk = 0;
   a.row_tiles = RT;
   a.rtw = RTW;
@@ -361,8 +371,9 @@ int32_t kvq_choose_num_splits_mq(const kvq_cache_t *cache, int32_t num_seqs, int
   if (st != KVQ_OK) return st;
   if (num_seqs <= 0 || max_context_len < 1 || num_query_tokens < 1 || num_query_tokens > kMaxQueryTokens)
     return KVQ_ERR_INVALID_ARG;
+  const int G = num_q_heads / cache->num_kv_heads;
   return choose_splits(cache->dtype, num_seqs, cache->num_kv_heads, cache->head_dim, max_context_len, device_cus(),
-                       row_tiles_for(num_query_tokens, num_q_heads / cache->num_kv_heads));
+                       row_tiles_for(num_query_tokens, G), chunks_for(num_query_tokens, G));
 }
 
 int kvq_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,

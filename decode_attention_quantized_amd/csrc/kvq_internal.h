@@ -29,8 +29,10 @@ struct DecodeArgs {
   int max_blocks, max_context_len, S, Hq, Hkv, G, NB, NS, cpp, D;
   int waves;                      // wavefronts per split workgroup (1, 2, 4 or 8)
   int nq;                         // query tokens per sequence (q [S][nq][Hq][D], causal among them)
+  int qchunk;                     // query tokens per workgroup (the chunk; nq is cut into chunks)
+  int chunks;                     // ceil(nq / qchunk)
   int int_qk;                     // 1: integer Q.K (Q quantized per 32 values like the cache; q8_0 only)
-  int row_tiles;                  // ceil(nq * G / 16): 16-row MFMA tiles of (query token, head) pairs
+  int row_tiles;                  // ceil(qchunk * G / 16): 16-row MFMA tiles of (query token, head) pairs
   int rtw;                        // row tiles per workgroup (1, 2 or 4; its waves split into rtw groups)
   int row_groups;                 // ceil(row_tiles / rtw): workgroups per (split, KV head, sequence)
 };

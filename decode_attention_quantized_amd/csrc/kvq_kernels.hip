@@ -411,15 +411,16 @@ __device__ __forceinline__ void write_new_bf16(const DecodeArgs &a, int64_t page
 }
 
 // Q operand for several query tokens: MFMA row r = 16 * rt + n16 of KV head h is the pair
-// (query token r / G, head h * G + r % G); rows past nq * G read zeros.
+// (query token c0 + r / G, head h * G + r % G) of the workgroup's chunk (query tokens c0 ..
+// c0 + n_here - 1); rows past n_here * G read zeros.
 template <int D>
-__device__ __forceinline__ void load_q_mq(const DecodeArgs &a, int s, int h, int rt, int n16, int q4,
-                                          u4_t (&qraw)[D / 32]) {
+__device__ __forceinline__ void load_q_mq(const DecodeArgs &a, int s, int h, int rt, int c0, int n_here, int n16,
+                                          int q4, u4_t (&qraw)[D / 32]) {
   const uint16_t *base = a.q + (int64_t)s * a.nq * a.Hq * D;
   const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), 0, a.nq * a.Hq * D * 2, 0x00020000);
   const int row = 16 * rt + n16;
-  const int i = row / a.G, g = row - i * a.G;
-  const int off = row < a.nq * a.G ? (((i * a.Hq + h * a.G + g) * D) + 8 * q4) * 2 : 0x40000000;
+  const int i = row / a.G, g = row - i * a.G;  // query token c0 + i of the chunk, head h * G + g
+  const int off = row < n_here * a.G ? ((((c0 + i) * a.Hq + h * a.G + g) * D) + 8 * q4) * 2 : 0x40000000;
 #pragma unroll
   for (int gg = 0; gg < D / 32; ++gg) qraw[gg] = ld16(r, off, gg * kGroup * 2);
 }
@@ -438,7 +439,7 @@ constexpr int merge_stride() { return (D / 16) * 256 + 32; }
 template <int D, int NW, bool MQ = false, int RTW = 1>
 __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h, int j, int wave, int n16, int q4,
                                               float m_run, float l_run, const f4_t (&acc)[D / 16], float *merge,
-                                              int rt = 0) {
+                                              int rt = 0, int c0 = 0, int n_here = 1) {
   constexpr int NT = D / 16;
   constexpr int ST = merge_stride<D>();
   constexpr int NWP = NW / RTW;  // waves per row tile
@@ -460,7 +461,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
     if (q4 == 0 && n16 < G) a.ml[row0 + (int64_t)n16 * a.NS] = make_float2(m_run, l_run);
   } else {
     float *mine = merge + wave * ST;
-    const int rows_here = MQ ? min(a.nq * G - 16 * rt, 16) : G;  // real rows of this tile
+    const int rows_here = MQ ? min(n_here * G - 16 * rt, 16) : G;  // real rows of this tile
     if (4 * q4 < rows_here) {  // lanes that hold a real row
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) *reinterpret_cast<f4_t *>(mine + (jt * 64 + lane) * 4) = acc[jt];
@@ -498,7 +499,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
     const float2 *ml_base;
     const float *o_base;
     if constexpr (MQ) {
-      // tile row 16 rt + r is (query token (16 rt + r) / G, head h G + (16 rt + r) % G) of sequence s
+      // tile row 16 rt + r is (query token c0 + (16 rt + r) / G, head h G + (16 rt + r) % G)
       const int64_t seq0 = (int64_t)s * a.nq * a.Hq * a.NS;  // first partial row of the sequence
       rows_valid = a.nq * a.Hq * a.NS;
       ml_base = a.ml + seq0;
@@ -507,7 +508,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * rt + 4 * q4 + i;
         const int t = row / G, g = row - t * G;
-        row_off[i] = row < a.nq * G ? (t * a.Hq + h * G + g) * a.NS + j : rows_valid;
+        row_off[i] = row < n_here * G ? ((c0 + t) * a.Hq + h * G + g) * a.NS + j : rows_valid;
       }
     } else {
       rows_valid = (G - 1) * a.NS + 1;  // rows from head 0 through head G - 1 of this split
@@ -583,8 +584,14 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   const int rg = MQ ? (blockIdx.x / a.NS) % a.row_groups : 0;
   const int rt = rg * RTW + rl;
   const int h = (blockIdx.x / (a.NS * (MQ ? a.row_groups : 1))) % a.Hkv;
-  const int s = blockIdx.x / (a.NS * (MQ ? a.row_groups : 1) * a.Hkv);
-  const int L = max(0, min(context_lens[s], a.max_context_len));
+  // MQ: the query chunk (tokens c0 .. c0 + n_here - 1 of the sequence's nq), between KV head and
+  // sequence; it attends over the keys up to its last query token
+  const int c = MQ ? (blockIdx.x / (a.NS * a.row_groups * a.Hkv)) % a.chunks : 0;
+  const int s = blockIdx.x / (a.NS * (MQ ? a.row_groups * a.chunks : 1) * a.Hkv);
+  const int c0 = c * (MQ ? a.qchunk : 1);
+  const int n_here = MQ ? min(a.qchunk, a.nq - c0) : 1;
+  const int L_full = max(0, min(context_lens[s], a.max_context_len));
+  const int L = MQ ? max(0, L_full - a.nq + c0 + n_here) : L_full;
   const int P = (L + kPage - 1) / kPage;
   const int p0 = j * a.cpp;
   const int p1 = min(p0 + a.cpp, P);
@@ -640,9 +647,9 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   const int k_last = (n_units - 1) / NWP;
   // MQ: the lane's row sees keys 0 .. L - nq + token (causal among the query tokens)
   int L_row = L;
-  if constexpr (MQ) L_row = L - a.nq + (16 * rt + n16) / a.G + 1;
+  if constexpr (MQ) L_row = L_full - a.nq + c0 + (16 * rt + n16) / a.G + 1;
   u4_t qraw[NG];
-  if constexpr (MQ) load_q_mq<D>(a, s, h, rt, n16, q4, qraw);
+  if constexpr (MQ) load_q_mq<D>(a, s, h, rt, c0, n_here, n16, q4, qraw);
   else load_q<D>(a, s, h, n16, q4, qraw);
   u2_t knew, vnew;
   load_new_rows<D>(a, s, h, own_new, lane, knew, vnew);
@@ -931,7 +938,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) acc[jt] *= f;
   }
-  write_partial<D, NW, MQ, RTW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, rt);
+  write_partial<D, NW, MQ, RTW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, rt, c0, n_here);
 }
 
 // ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
@@ -1086,7 +1093,11 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
   const int64_t orow = ((int64_t)s * HQ + hq);
   const int64_t base = orow * a.NS;
 
-  const int Lc = a.context_lens[s];  // (the loads below do not depend on it)
+  // (the loads below do not depend on it) the row's query chunk attends over the keys up to its
+  // last query token: the context length that sets the row's splits
+  const int Lc = a.context_lens[s];
+  const int qi = hq / a.Hq;  // query token of the row
+  const int c0 = qi - qi % a.qchunk, n_here = min(a.qchunk, a.nq - c0);
   float m = -INFINITY, l = 0.0f, o = 0.0f;
   auto fold = [&](float mj, float lj, float oj) {
     if (mj == -INFINITY) return;
@@ -1110,7 +1121,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
       mlv[u] = make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
       ov[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, c * 4, jj * D * 4, 0));
     }
-    const int L = max(0, min(Lc, a.max_context_len));
+    const int L = max(0, min(max(0, min(Lc, a.max_context_len)) - a.nq + c0 + n_here, a.max_context_len));
     const int nsa = min(a.NS, ((L + kPage - 1) / kPage + a.cpp - 1) / a.cpp);  // splits with pages
 #pragma unroll
     for (int u = 0; u < UNR; ++u)
@@ -1187,7 +1198,7 @@ static void launch_split_nw(const DecodeArgs &a, hipStream_t stream) {
 // KV head, sequence).
 template <int D, int FMT>
 static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
-  const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.row_groups * a.NS);
+  const unsigned grid = (unsigned)((int64_t)a.S * a.chunks * a.Hkv * a.row_groups * a.NS);
   const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);
   if (a.rtw == 4)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);

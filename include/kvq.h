@@ -168,8 +168,11 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
                          void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Decode attention for num_query_tokens (n_q, 1..64) query tokens per sequence, causal among them
- * (INT8 cache only).  The query tokens of sequence s are its last n_q positions L-n_q .. L-1
+ * Decode attention for num_query_tokens (n_q, 1..65536) query tokens per sequence, causal among
+ * them (INT8 caches).  Large n_q is a prompt section over the cache: half-the-memory page,
+ * section "Read the prompt using a small temporary buffer": a new prompt section attends to the
+ * cached keys before it and causally to itself, the parts combined with their attention weights;
+ * here straight from the INT8 pages (no converted copy), the combination being the split merge.  The query tokens of sequence s are its last n_q positions L-n_q .. L-1
  * (L = context_lens[s], which includes them): query token i attends to the keys at positions
  * 0 .. L-n_q+i.  n_q == 1 is kvq_decode_attention.
  *   q            device, bfloat16 [num_seqs][n_q][num_q_heads][D], 16-byte aligned.
@@ -180,8 +183,11 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
  *   other arguments as kvq_decode_attention.  A query token with no visible key (L < n_q) gets
  *   out = 0 and lse = -inf.  Returns KVQ_ERR_UNSUPPORTED for a BF16 cache with n_q > 1.
  * The (query token, head) pairs of one KV head form the rows of 16-row MFMA tiles; up to 4
- * tiles (n_q * G <= 64) share one workgroup and one read of each page, each further 4 tiles
- * read the sequence's pages again.
+ * tiles (64 rows, 64 / G query tokens) share one workgroup and one read of each page.  Longer
+ * runs are cut into chunks of 64 / G query tokens, each chunk attending over the keys up to its
+ * own last token, so each chunk reads its prefix once.  One sequence's q block and partials must
+ * stay below 2 GiB (n_q * Hq * D * 2 and n_q * Hq * splits * D * 4 bytes), else
+ * KVQ_ERR_INVALID_ARG.
  */
 int kvq_decode_attention_mq(const kvq_cache_t *cache, const void *q, int32_t num_query_tokens,
                             const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,

@@ -143,7 +143,7 @@ def test_decode_mq_rejects_invalid_arguments():
         return K.lib.kvq_decode_attention_mq(ctypes.byref(desc), q, nq, FAKE, 32, FAKE, 512, 1, Hq, ns, FAKE, None,
                                              FAKE, wsb, None)
     assert mq(d, nq=0) == -1
-    assert mq(d, nq=65) == -1
+    assert mq(d, nq=65537) == -1
     assert mq(d, q=None) == -1
     assert mq(d, Hq=25) == -1
     assert mq(_desc(dtype=K.BF16, ks=None, vs=None)) == -2      # INT8 cache only for n_q > 1

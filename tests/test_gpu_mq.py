@@ -96,5 +96,18 @@ def test_mq_rejects_bad_arguments():
     assert ei.value.status == -2  # several query tokens need the INT8 cache
     g8 = K.Cache("int8", 8, 2, 128)
     with pytest.raises(K.KvqError) as ei:
-        K.decode_mq(g8, torch.zeros((1, 65, 4, 128), dtype=torch.bfloat16, device="cuda"), bt, cl, 20, 2)
+        K.decode_mq(g8, torch.zeros((1, 65537, 4, 128), dtype=torch.bfloat16, device="cuda"), bt, cl, 20, 2)
     assert ei.value.status == -1
+
+
+@pytest.mark.parametrize("nq", [11, 40, 100, 257])
+def test_prompt_sections(nq):
+    """Runs of query tokens longer than one workgroup's 64 rows (a prompt section over the cache):
+    cut into chunks, each attending over the keys up to its own last token."""
+    pair, q, bt, lens = _problem(2300 + nq, [nq, nq + 5, 700, 1500], 24, 4, 256, nq)
+    _check(pair, q, bt, lens, [1, 4, 0], f"prompt section nq={nq}")
+
+
+def test_prompt_section_dense_geometry():
+    pair, q, bt, lens = _problem(2400, [300, 1000], 32, 8, 128, 64)
+    _check(pair, q, bt, lens, [2, 0], "prompt section G=4 D=128 nq=64")
