@@ -330,7 +330,7 @@ def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
     cfg = W.CONFIGS[3]
     layer_bytes = algorithmic_bytes(np.array(cfg.context_lens), cfg.num_kv_heads, cfg.head_dim, "int8")
     rec = {
-        "kernel": "decode_split_i8_kernel<256,4,false,0>",
+        "kernel": "decode_split_i8_kernel<256, 4, 0, 0>",
         "workload": "long-32k layer: batch 1, context 32768, 24/4 heads, head_dim 256",
         "kernel_source_sha256": kernel_source_digest(),
         "fetch_kib_per_launch_raw": round(fs / 1024, 1), "write_kib_per_launch_raw": round(ws_ / 1024, 1),
@@ -341,7 +341,7 @@ def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
         "dispatches": {"split_fetch": nfs, "split_write": nws, "copy_fetch": nfc, "copy_write": nwc},
     }
     text = [
-        "# HBM traffic: decode_split_i8_kernel<256,4,false,0> (q8_0), long-32k layer (context 32768, 24/4 heads, D 256)",
+        "# HBM traffic: decode_split_i8_kernel<256, 4, 0, 0> (q8_0), long-32k layer (context 32768, 24/4 heads, D 256)",
         "",
         "Two counter runs of the same program, one counter each (commands from the repository root",
         "on one MI355X; `$REPO` is the repository root):",
@@ -548,7 +548,7 @@ def main():
             "algorithmic_bytes_per_step": r["step_bytes"],
         },
         "roofline": {
-            "kernel": "decode_split_kernel<256,4,int8>" if D == 256 else "decode_split_kernel<128,4,int8>",
+            "kernel": "decode_split_i8_kernel<256, 4, 0, 0>" if D == 256 else "decode_split_i8_kernel<128, 4, 0, 0>",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
