@@ -1070,21 +1070,47 @@ void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_ta
 
 // ------------------------------------------------------------------ decode: merge
 //
-// Workgroup (64-channel chunk, output row, sequence) of kMergeWaves wavefronts (an output row is a
-// (query token, query head) pair; one query token per sequence unless nq > 1); wave w takes
-// splits w, w + kMergeWaves, ... and folds them into a running (m, l, o) with the same rescaling
-// as the online softmax, so the partials are read in one pass (no separate pass for the global
-// maximum).  Only the splits that hold pages are folded (their count follows from the context
-// length, which is read alongside the first partials).  The waves' results are then folded the
-// same way through LDS:  out = o / l;  lse = ln 2 * (m + log2 l).
-constexpr int kMergeWaves = 4;
+// One wavefront per (64-channel chunk, output row, sequence); an output row is a (query token,
+// query head) pair (one query token per sequence unless nq > 1).  The splits are taken 64 at a
+// time: lane j loads split j's (m, l) and every lane loads its channel of all 64 partial outputs,
+// all in one round trip.  The block's maximum and weights w_j = 2^(m_j - M) come from wave
+// reductions, each lane folds the 64 partials with the weights broadcast from their lanes, and
+// blocks beyond the first (more than 64 splits) are folded with the online softmax's rescaling.
+// Only the splits that hold pages count (their number follows from the row's context length,
+// read alongside the partials):  out = o / l;  lse = ln 2 * (M + log2 l).
+constexpr int kMergeBlock = 64;
+
+// Reductions over a wavefront: DPP within each 16-lane row (pairs, quads, half rows, rows), then
+// the four row results read into scalars.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row_lane(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  return fmaxf(fmaxf(row_lane(x, 0), row_lane(x, 16)), fmaxf(row_lane(x, 32), row_lane(x, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return (row_lane(x, 0) + row_lane(x, 16)) + (row_lane(x, 32) + row_lane(x, 48));
+}
 
 template <int D>
-__global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int NCH = D / 64;
-  constexpr int UNR = 16;  // partials requested together per wave (one round trip up to 64 splits)
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x;
   const int HQ = a.Hq * a.nq;  // output rows per sequence: (query token, query head)
   const int chunk = blockIdx.x % NCH;
   const int hq = (blockIdx.x / NCH) % HQ;
@@ -1092,61 +1118,53 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
   const int c = chunk * 64 + lane;
   const int64_t orow = ((int64_t)s * HQ + hq);
   const int64_t base = orow * a.NS;
-
-  // (the loads below do not depend on it) the row's query chunk attends over the keys up to its
-  // last query token: the context length that sets the row's splits
+  // buffer loads over this row's partials (past NS they return 0 and are masked below)
+  const auto rml = __builtin_amdgcn_make_buffer_rsrc(a.ml + base, 0, a.NS * 8, 0x00020000);
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc(a.o_part + base * D, 0, a.NS * D * 4, 0x00020000);
+  // the row's query chunk attends over the keys up to its last query token: the context length
+  // that sets the row's splits
   const int Lc = a.context_lens[s];
   const int qi = hq / a.Hq;  // query token of the row
   const int c0 = qi - qi % a.qchunk, n_here = min(a.qchunk, a.nq - c0);
-  float m = -INFINITY, l = 0.0f, o = 0.0f;
-  auto fold = [&](float mj, float lj, float oj) {
-    if (mj == -INFINITY) return;
-    const float mn = fmaxf(m, mj);
-    const float a0 = exp2_w(m - mn), a1 = exp2_w(mj - mn);  // (m = -inf gives a0 = 0)
-    o = fmaf(o, a0, oj * a1);
-    l = fmaf(l, a0, lj * a1);
-    m = mn;
-  };
-  // buffer loads over this head's partials: vector loads (a uniform address would otherwise
-  // become a scalar load waited on one at a time)
-  const auto rml = __builtin_amdgcn_make_buffer_rsrc(a.ml + base, 0, a.NS * 8, 0x00020000);
-  const auto ro = __builtin_amdgcn_make_buffer_rsrc(a.o_part + base * D, 0, a.NS * D * 4, 0x00020000);
-  for (int j0 = wave; j0 < a.NS; j0 += kMergeWaves * UNR) {
-    float2 mlv[UNR];
-    float ov[UNR];
+  float M = -INFINITY, l = 0.0f, o = 0.0f;
+  for (int j0 = 0; j0 < a.NS; j0 += kMergeBlock) {
+    const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, lane * 8, j0 * 8, 0));
+    float ov[kMergeBlock];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int jj = j0 + u * kMergeWaves;  // (past NS: the resources return 0; skipped below)
-      const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, 0, jj * 8, 0));
-      mlv[u] = make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
-      ov[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, c * 4, jj * D * 4, 0));
-    }
-    const int L = max(0, min(max(0, min(Lc, a.max_context_len)) - a.nq + c0 + n_here, a.max_context_len));
+    for (int u = 0; u < kMergeBlock; ++u)
+      ov[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, c * 4, (j0 + u) * D * 4, 0));
+    // (kept in the loop, after the loads: hoisted out of it, the wait for the context length
+    // would come before the partials are requested)
+    int Lk = Lc;
+    asm volatile("" : "+s"(Lk));
+    const int L = max(0, min(max(0, min(Lk, a.max_context_len)) - a.nq + c0 + n_here, a.max_context_len));
     const int nsa = min(a.NS, ((L + kPage - 1) / kPage + a.cpp - 1) / a.cpp);  // splits with pages
+    // splits past nsa were not written by this call: their (m, l, o) are masked, never multiplied
+    const int nb = nsa - j0;
+    const bool valid = lane < nb;
+    const float mj = valid ? __uint_as_float(w[0]) : -INFINITY;
+    const float Mn = fmaxf(M, wave_max(mj));
+    const float Mr = (Mn == -INFINITY) ? 0.0f : Mn;  // (no key yet: any finite reference)
+    const float alpha = exp2_w(M - Mr);                // M = -inf: 0
+    const float wj = exp2_w(mj - Mr);                  // mj = -inf: 0
+    l = fmaf(l, alpha, wave_sum(valid ? wj * __uint_as_float(w[1]) : 0.0f));
+    float acc = o * alpha;
+    if (nb >= kMergeBlock) {
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
-      if (j0 + u * kMergeWaves < nsa) fold(mlv[u].x, mlv[u].y, ov[u]);
-  }
-  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves], s_o[kMergeWaves][64];
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_l[wave] = l;
-  }
-  s_o[wave][lane] = o;
-  __syncthreads();
-  if (wave == 0) {
-    m = -INFINITY;
-    l = 0.0f;
-    o = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) fold(s_m[w], s_l[w], s_o[w][lane]);
-    if (m == -INFINITY) {  // no split holds a page: empty context
-      a.out[orow * D + c] = 0.0f;
-      if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = -INFINITY;
+      for (int u = 0; u < kMergeBlock; ++u) acc = fmaf(row_lane(wj, u), ov[u], acc);
     } else {
-      a.out[orow * D + c] = o / l;
-      if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = kLn2 * (m + log2f(l));
+#pragma unroll
+      for (int u = 0; u < kMergeBlock; ++u) acc = fmaf(row_lane(wj, u), (u < nb) ? ov[u] : 0.0f, acc);
     }
+    o = acc;
+    M = Mn;
+  }
+  if (M == -INFINITY) {  // no split holds a key: empty context
+    a.out[orow * D + c] = 0.0f;
+    if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = -INFINITY;
+  } else {
+    a.out[orow * D + c] = o / l;
+    if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = kLn2 * (M + log2f(l));
   }
 }
 
@@ -1234,8 +1252,8 @@ hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t strea
 
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hq * a.nq * (a.D / 64));
-  if (a.D == 256) hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, a);
-  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(kMergeWaves * 64), 0, stream, a);
+  if (a.D == 256) hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(64), 0, stream, a);
+  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
