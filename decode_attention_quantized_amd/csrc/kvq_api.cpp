@@ -68,20 +68,24 @@ int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 // workgroup per CU evens out the longest ones (the host sees only the maximum length).  Both
 // choices come from split-count sweeps of the INT8 and BF16 kernels on 256 CUs (one sequence at
 // 4K and 32K tokens, 4 sequences of 2K-32K, 32 sequences of 512-8K).
-// (row_tiles > 1: several query tokens per sequence, one workgroup per 16-row tile of (query
-// token, head) pairs; the tiles of one split count as a batch.)
+// Several query tokens per sequence (row_tiles > 1): a workgroup holds rtw 16-row tiles of
+// (query token, head) pairs, and the count is set by the workgroups per (sequence, KV head), as
+// for one query token.  Workgroups of 4 tiles (one wave per tile) keep no merge scratch in LDS,
+// so two fit on a CU and count as two slots.  Prompt sections (several query chunks) get at
+// least four rounds of workgroups, so that the last, partly filled round is short.  Sweeps at
+// 32K: 8 query tokens run best at 128 splits (two workgroups per CU); a 2048-token section takes
+// 6.3 ms at 1 split, 5.5 ms at 2 and 5.1 ms at 4 (this rule gives 3).
 int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus, int row_tiles = 1,
                   int chunks = 1) {
   (void)dtype;
   (void)D;
   const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
   if (max_pages <= 0) return 1;
-  // several query tokens: a workgroup holds rtw row tiles (its LDS then leaves room for one
-  // workgroup per CU), so the count is set by the workgroups per (sequence, KV head), as for one
-  // query token
   const int rtw = rtw_for(row_tiles), groups = (row_tiles + rtw - 1) / rtw * chunks;
+  const int64_t slots = (int64_t)(row_tiles > 1 && rtw == 4 ? 2 : 1) * cus;  // workgroups resident at once
   const int64_t base = (int64_t)S * Hkv * groups;
-  const int64_t target_wg = ((int64_t)S * groups > 1 ? 2LL : 1LL) * cus;
+  int64_t target_wg = ((int64_t)S * groups > 1 ? 2LL : 1LL) * slots;
+  if (chunks > 1 && target_wg < 4 * slots) target_wg = 4 * slots;
   int64_t ns = (target_wg + base - 1) / base;
   const int min_pages = 8;
   const int64_t cap = (max_pages + min_pages - 1) / min_pages;

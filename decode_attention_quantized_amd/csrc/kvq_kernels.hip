@@ -450,7 +450,32 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
   l_run = rows_sum(l_run);
   const int64_t row0 = ((int64_t)s * a.Hq + (int64_t)h * G) * a.NS + j;  // partial of head h*G + 0
   static_assert(!(MQ && NW == 1), "several query tokens use the LDS merge path");
-  if constexpr (NW == 1) {
+  if constexpr (MQ && NWP == 1) {
+    // One wave per row tile: the tile's partial sits in this wave's registers, no LDS merge.
+    // Tile row r is (query token c0 + (16 rt + r) / G, head h G + (16 rt + r) % G); rows past the
+    // chunk's n_here * G real rows map past the end of the resources and their stores are dropped.
+    const int64_t seq0 = (int64_t)s * a.nq * a.Hq * a.NS;  // first partial row of the sequence
+    const int rows_valid = a.nq * a.Hq * a.NS;
+    auto row_offset = [&](int r) -> int {
+      const int row = 16 * rt + r;
+      const int t = row / G, g = row - t * G;
+      return row < n_here * G ? ((c0 + t) * a.Hq + h * G + g) * a.NS + j : rows_valid;
+    };
+    if (q4 == 0) {  // (m, l) of row n16 (the same in the row's 4 lanes)
+      const auto rml = __builtin_amdgcn_make_buffer_rsrc(a.ml + seq0, 0, rows_valid * 8, 0x00020000);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2_t, make_float2(m_run, l_run)), rml,
+                                            row_offset(n16) * 8, 0, 0);
+    }
+    const auto ro = __builtin_amdgcn_make_buffer_rsrc(a.o_part + seq0 * D, 0, rows_valid * D * 4, 0x00020000);
+    int row_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row_off[i] = row_offset(4 * q4 + i);
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[jt][i]), ro, (row_off[i] * D + 16 * jt + n16) * 4, 0, 0);
+  } else if constexpr (NW == 1) {
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt)
 #pragma unroll
@@ -1217,9 +1242,9 @@ static void launch_split_nw(const DecodeArgs &a, hipStream_t stream) {
 template <int D, int FMT>
 static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.chunks * a.Hkv * a.row_groups * a.NS);
-  const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);
-  if (a.rtw == 4)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
+  const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);  // LDS merge of a tile's waves
+  if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
   else if (a.rtw == 2)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
   else
