@@ -966,6 +966,259 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   write_partial<D, NW, MQ, RTW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, s_merge, rt, c0, n_here);
 }
 
+// ---- INT8 cache (q8_0), several query tokens in 4 row tiles: the waves walk the pages together
+//
+// Workgroup (split, KV head, query chunk, sequence) of 4 waves, one 16-row tile of (query token,
+// head) pairs each: the rows, grid and partials of decode_split_i8_kernel<D, 4, 4, 0>.  Instead
+// of every wave loading and converting every page, the workgroup loads each page once: thread t
+// takes the page's 16-byte code chunks t, t + 256, ... (K chunks first, then V; D / 128 per
+// thread), converts them to the f16 MFMA fragments and stores them in LDS, and waves 0 and 1 stage
+// the K and V scale tiles.  After one barrier every wave reads the fragments of all groups from
+// LDS and runs the decode kernel's page step on its own tile (Q.K per group and fp16 scale,
+// online softmax, P' = p * s_v as f16 hi + lo, P.V).  LDS holds two pages, so the stores of page
+// k + 1 never meet the reads of page k - 1; each thread holds a quarter or an eighth of a page in
+// registers, so NBUF pages are in flight at little register cost.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void section_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
+  constexpr int NW = 4;                  // waves = row tiles
+  constexpr int NG = D / kGroup;         // scale groups
+  constexpr int NT = D / 16;             // output tiles
+  constexpr int PAGE_B = kPage * D;      // bytes of one code page
+  constexpr int CH = PAGE_B / 16;        // 16-byte chunks per code page
+  constexpr int CPT = 2 * CH / (NW * 64);  // chunks per thread per page (K and V together)
+  constexpr int SCALE_B = kPage * NG * 2;  // bytes of one scale tile
+  constexpr int SDW = SCALE_B / 4;
+  constexpr int NBUF = 4;                // pages in flight
+  static_assert(CPT >= 1 && (NBUF & 1) == 0, "page split and LDS double buffer");
+  __shared__ __attribute__((aligned(16))) h8_t s_k[2][NG][64];     // K fragments [group][lane]
+  __shared__ __attribute__((aligned(16))) u4_t s_v[2][NT][64];     // V operands [tile][lane] (codes twice)
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[2][2][SDW];  // K, V scale tiles, token-quad-major
+  __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];   // rescale factors, per row
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);  // (0 .. 3: lets the compiler fix each chunk's plane)
+  const int rt = wave;  // this wave's row tile
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int j = blockIdx.x % a.NS;
+  const int h = (blockIdx.x / (a.NS * a.row_groups)) % a.Hkv;
+  const int c = (blockIdx.x / (a.NS * a.row_groups * a.Hkv)) % a.chunks;
+  const int s = blockIdx.x / (a.NS * a.row_groups * a.chunks * a.Hkv);
+  const int c0 = c * a.qchunk;
+  const int n_here = min(a.qchunk, a.nq - c0);
+  const int L_full = max(0, min(a.context_lens[s], a.max_context_len));
+  const int L = max(0, L_full - a.nq + c0 + n_here);  // the chunk attends over keys 0 .. L - 1
+  const int P = (L + kPage - 1) / kPage;
+  const int p0 = j * a.cpp;
+  const int p1 = min(p0 + a.cpp, P);
+  if (p0 >= p1) return;  // empty split (uniform): nothing written, the merge skips it
+  const int n_units = p1 - p0;
+  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
+  auto page_of = [&](int k) -> int64_t {
+    const int blk = btrow[min(p0 + k, p1 - 1)];
+    return (int64_t)min(max(blk, 0), a.NB - 1) * a.Hkv + h;
+  };
+
+  // ---- this thread's share of a page: code chunks id = t + 256 ci (K if id < CH, else V; chunk
+  // cc of its plane is lane cc % 64's 16 bytes at 1 KiB offset cc / 64, i.e. the decode kernel's
+  // load cc / 64 of that lane), and one dword of a scale tile (wave 0: K, wave 1: V)
+  u4_t cb[NBUF][CPT];
+  uint32_t sb[NBUF];
+  auto issue = [&](int b, int k) {
+    const bool ok = k < n_units;  // (past the split: size-0 resources, the loads return zeros)
+    const int64_t page = page_of(k);
+#pragma unroll
+    for (int ci = 0; ci < CPT; ++ci) {
+      const int id0 = wave * 64 + NW * 64 * ci;  // the wave's first chunk (wave-uniform)
+      const bool is_v = id0 >= CH;
+      const auto r = page_rsrc(is_v ? a.vc : a.kc, page, PAGE_B, ok ? PAGE_B : 0);
+      cb[b][ci] = ld16(r, lane * 16, ((is_v ? id0 - CH : id0) >> 6) * 1024);
+    }
+    const auto rs = page_rsrc(wave == 1 ? (const void *)a.vs : (const void *)a.ks, page, SCALE_B,
+                              ok && wave < 2 ? SCALE_B : 0);
+    sb[b] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0);
+  };
+  // restaged scale dword of tile dword l (group-major [group][token] -> [token quad][group][token])
+  const int st_dw = (((lane & 7) >> 1) * NG + (lane >> 3)) * 2 + (lane & 1);
+  auto stage = [&](int b, int lb, int k) {
+#pragma unroll
+    for (int ci = 0; ci < CPT; ++ci) {
+      const int id0 = wave * 64 + NW * 64 * ci;
+      const bool is_v = id0 >= CH;
+      const int i = (is_v ? id0 - CH : id0) >> 6;  // the decode kernel's load index
+      const u4_t w = cb[b][ci];
+      if (!is_v) {
+        s_k[lb][2 * i][lane] = i8x8_to_h8(w[0], w[1]);
+        s_k[lb][2 * i + 1][lane] = i8x8_to_h8(w[2], w[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t v0, v1;
+          i8x4_to_f16(w[e], v0, v1);
+          s_v[lb][4 * i + e][lane] = u4_t{v0, v1, v0, v1};  // the P.V operand as it is read
+        }
+      }
+    }
+    // V scales of tokens past the chunk's context are stored as 0: those tokens have p = 0, but
+    // their codes and scales may be stale (even NaN).  Tile dword l holds tokens 2 (l % 8) and
+    // 2 (l % 8) + 1 of group l / 8.
+    uint32_t sw = sb[b];
+    if (wave == 1) {
+      const int lim = k < n_units ? min(L - (p0 + k) * kPage, kPage) : 0;
+      const int t0 = 2 * (lane & 7);
+      sw &= (t0 < lim ? 0xFFFFu : 0u) | (t0 + 1 < lim ? 0xFFFF0000u : 0u);
+    }
+    if (wave < 2 && lane < SDW) s_sc[lb][wave][st_dw] = sw;
+  };
+  auto lds_barrier = [] {  // LDS-only fences: the page loads in flight are not waited for
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  };
+
+  // Q first, then the first NBUF pages
+  u4_t qraw[NG];
+  load_q_mq<D>(a, s, h, rt, c0, n_here, n16, q4, qraw);
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) {  // (in page order, and before Q is waited for)
+    issue(b, b);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Q rescaled per row by 2^shift so that max |q| lies in [2^14, 2^15): exact in f16
+  int shift = 0;
+  {
+    float qmax = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qmax = fmaxf(qmax, fmaxf(fabsf(bf16_lo(qraw[g][e])), fabsf(bf16_hi(qraw[g][e]))));
+    qmax = rows_max(qmax);
+    if (qmax > 0.0f) {
+      int e2;
+      frexpf(qmax, &e2);
+      shift = 15 - e2;
+    }
+  }
+  h8_t qop[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qop[g][2 * e] = (_Float16)ldexpf(bf16_lo(qraw[g][e]), shift);
+      qop[g][2 * e + 1] = (_Float16)ldexpf(bf16_hi(qraw[g][e]), shift);
+    }
+  const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
+  // the lane's row (query token c0 + (16 rt + n16) / G) sees keys 0 .. L_row - 1
+  const int L_row = L_full - a.nq + c0 + (16 * rt + n16) / a.G + 1;
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f4_t acc[NT];
+#pragma unroll
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto scales = [&](int lb, int which, u2_t (&out)[NG]) {
+    const u4_t *src = reinterpret_cast<const u4_t *>(&s_sc[lb][which][q4 * NG * 2]);
+#pragma unroll
+    for (int i = 0; i < NG / 2; ++i) {
+      const u4_t w = src[i];
+      out[2 * i] = u2_t{w[0], w[1]};
+      out[2 * i + 1] = u2_t{w[2], w[3]};
+    }
+  };
+
+  // One page from LDS buffer lb: Q.K^T, one online-softmax update, P.V (the decode kernel's step).
+  auto process = [&](int lb, int k) {
+    // valid tokens of the page for this lane's row
+    const int lim_row = k < n_units ? min(max(L_row - (p0 + k) * kPage, 0), kPage) : 0;
+    u2_t ksc[NG];
+    scales(lb, 0, ksc);
+    f4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto scale_group = [&](int g, const f4_t &cg) {
+      const u2_t sw = ksc[g];
+      sc[0] = fma_h16lo(sw[0], cg[0], sc[0]);
+      sc[1] = fma_h16hi(sw[0], cg[1], sc[1]);
+      sc[2] = fma_h16lo(sw[1], cg[2], sc[2]);
+      sc[3] = fma_h16hi(sw[1], cg[3], sc[3]);
+      pin4(sc);
+    };
+    f4_t c_prev = mfma_f16(s_k[lb][0][lane], qop[0], f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+    for (int g = 1; g < NG; ++g) {
+      const f4_t cg = mfma_f16(s_k[lb][g][lane], qop[g], f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      scale_group(g - 1, c_prev);
+      c_prev = cg;
+    }
+    scale_group(NG - 1, c_prev);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim_row) ? sc[i] * cmul : -INFINITY;
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = rows_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = (m_new == m_run) ? 1.0f : exp2_w(m_run - m_use);
+    const bool grew = alpha != 1.0f && m_run != -INFINITY;
+    float p[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2_w(x[i] - m_use);
+      psum += p[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(grew)) {  // some row's maximum grew: rescale its accumulator rows
+      if (q4 == 0) s_alpha[wave][n16] = alpha;
+      const f4_t ar = *reinterpret_cast<const f4_t *>(&s_alpha[wave][4 * q4]);
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) acc[jt] *= ar;
+    }
+    // P.V: P' = p * s_v per (token, group) as f16 hi + lo times the exact f16 V codes (the V
+    // scales of tokens past the chunk's context were staged as 0)
+    u2_t vsc[NG];
+    scales(lb, 1, vsc);
+    const h2_t ph01 = {(_Float16)p[0], (_Float16)p[1]}, ph23 = {(_Float16)p[2], (_Float16)p[3]};
+    const h2_t pl01 = {(_Float16)(p[0] - (float)ph01[0]), (_Float16)(p[1] - (float)ph01[1])};
+    const h2_t pl23 = {(_Float16)(p[2] - (float)ph23[0]), (_Float16)(p[3] - (float)ph23[1])};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const u2_t sv = vsc[g];
+      const uint32_t w01 = sv[0], w23 = sv[1];
+      const h2_t s01 = __builtin_bit_cast(h2_t, w01), s23 = __builtin_bit_cast(h2_t, w23);
+      const h2_t hi01 = ph01 * s01, hi23 = ph23 * s23;
+      const h2_t lo01 = __builtin_elementwise_fma(pl01, s01, __builtin_elementwise_fma(ph01, s01, -hi01));
+      const h2_t lo23 = __builtin_elementwise_fma(pl23, s23, __builtin_elementwise_fma(ph23, s23, -hi23));
+      const h8_t pp = __builtin_bit_cast(h8_t, u4_t{__builtin_bit_cast(uint32_t, hi01), __builtin_bit_cast(uint32_t, hi23),
+                                                   __builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jt = 2 * g + jj;
+        acc[jt] = mfma_f16(pp, __builtin_bit_cast(h8_t, s_v[lb][jt][lane]), acc[jt]);
+      }
+    }
+  };
+
+  // Step k: one barrier (page k is in LDS buffer k % 2, and every wave is done with page k - 1),
+  // then every wave's step on its tile for page k together with the staging of page k + 1 (its
+  // registers, buffer (k + 1) % NBUF, into LDS buffer (k + 1) % 2, which held page k - 1), so
+  // that the conversion overlaps the matrix products; the register buffer is then refilled with
+  // page k + 1 + NBUF.  The trip count is the same for every wave and a multiple of NBUF with no
+  // early exit: pages past the split's end read zeros and are fully masked (p = 0), which keeps
+  // the buffers in fixed registers and the waits for each page exact.
+  stage(0, 0, 0);
+  issue(0, NBUF);
+  for (int k0 = 0; k0 < n_units; k0 += NBUF) {
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+      const int k = k0 + b;
+      lds_barrier();
+      process(b & 1, k);
+      stage((b + 1) % NBUF, (b + 1) & 1, k + 1);
+      issue((b + 1) % NBUF, k + 1 + NBUF);
+    }
+  }
+  write_partial<D, NW, true, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, nullptr, rt, c0, n_here);
+}
+
 // ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
 __device__ __forceinline__ f4_t mfma16_bf16(s4_t a, s4_t b, f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -1243,7 +1496,9 @@ template <int D, int FMT>
 static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.chunks * a.Hkv * a.row_groups * a.NS);
   const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);  // LDS merge of a tile's waves
-  if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
+  if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
+    hipLaunchKernelGGL((section_i8_kernel<D>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
+  else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
   else if (a.rtw == 2)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
