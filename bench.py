@@ -44,7 +44,7 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=3, help="workload id (3 = 32K context, 16 layers)")
     p.add_argument("--splits", type=int, default=0, help="split count (0 = the library's choice)")
@@ -399,6 +399,28 @@ def cpu_baseline(host, states_int8, budget_s):
     return elapsed, nbytes, layers_done, max_err, within
 
 
+def cpu_baseline_one_thread(host):
+    """The same oracle work for the first layer on one host thread: (seconds, algorithmic bytes)."""
+    import oracle as O
+
+    lay, k, v, q = host[0]
+    cfg = lay.cfg
+    oc = O.OracleCache.empty("int8", lay.num_blocks, cfg.num_kv_heads, cfg.head_dim)
+    pre, stp = lay.prefill_rows(), lay.step_rows()
+    O.kv_write(oc, k[pre], v[pre], lay.slots[pre])
+    n0 = O.num_threads()
+    O.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        O.kv_write(oc, k[stp], v[stp], lay.slots[stp])
+        O.decode(oc, q, lay.block_tables, lay.context_lens)
+        el = time.perf_counter() - t0
+    finally:
+        O.set_num_threads(n0)
+    log(f"oracle layer 1 on one thread: {el:.2f}s")
+    return el, algorithmic_bytes(lay.context_lens, cfg.num_kv_heads, cfg.head_dim, "int8")
+
+
 FLUSH_BYTES = 512 << 20  # written between steps when the whole cache fits in the 256 MB MALL
 
 
@@ -598,6 +620,9 @@ def main():
             "sample": f"{nl} of {n_layers} layers: kv_write of the step token + fp64 decode of all {S * Hq} "
                       f"query rows per layer ({el:.1f} s)",
         }
+        el1, nb1 = cpu_baseline_one_thread(host)
+        out["cpu_baseline"]["one_thread"] = {"value": round(nb1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                             "sample": f"layer 1 of {n_layers} ({el1:.1f} s)"}
         out["parity_sample"] = {"layers": nl, "max_abs_err": max_err, "within_tolerance": within}
     print(json.dumps(out), flush=True)
 

@@ -67,6 +67,7 @@ def lib():
                                               P, P]
         L.oracle_quantize_rows_f32.argtypes = [P, i64, i32, P, P]
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -284,3 +285,8 @@ def dequantized_rows(cache: OracleCache, which: str) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's OpenMP loops use from now on (timing only; results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))

@@ -436,10 +436,12 @@ void oracle_quantize_rows_f32(const uint16_t *x, int64_t nrows, int n, int8_t *c
   for (int64_t r = 0; r < nrows; ++r) oracle_quantize_row_f32(x + r * n, n, codes + r * n, scales + r);
 }
 
-/* Thread count OpenMP will use (for reporting). */
+/* Thread count OpenMP will use (for reporting), and a way to change it (timing at one thread). */
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif
