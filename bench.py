@@ -163,10 +163,13 @@ def time_int_qk(torch, K, layers, S, Hq, mcl, ns, n_layers, steps, warmup):
     exact f16 Q.K and with integer Q.K, at the same split count; graph replay."""
     res = {}
     ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
+    # outputs of their own: each layer's out / lse keep the fused step's result, which the parity
+    # sample compares with the oracle
+    outs = [(torch.empty_like(L.out), torch.empty_like(L.lse)) for L in layers]
     for name, iq in (("f16_qk", False), ("int8_qk", True)):
         def step():
-            for L in layers:
-                K.decode(L.cache, L.q, L.bt, L.lens, mcl, ns, out=L.out, lse=L.lse, workspace=ws, int_qk=iq)
+            for L, (o, l) in zip(layers, outs):
+                K.decode(L.cache, L.q, L.bt, L.lens, mcl, ns, out=o, lse=l, workspace=ws, int_qk=iq)
         ms, _ = time_step(torch, step, steps, warmup, False)
         res[name + "_us_per_step"] = round(ms * 1e3, 1)
         log(f"attention only ({name}): {ms * 1e3:.1f} us/step")
@@ -624,6 +627,8 @@ def main():
         out["cpu_baseline"]["one_thread"] = {"value": round(nb1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                                              "sample": f"layer 1 of {n_layers} ({el1:.1f} s)"}
         out["parity_sample"] = {"layers": nl, "max_abs_err": max_err, "within_tolerance": within}
+        log(f"parity sample ({nl} layers, fused step against the oracle): max abs err {max_err:.3e}, "
+            + ("within tolerance" if within else "OUT OF TOLERANCE"))
     print(json.dumps(out), flush=True)
 
 

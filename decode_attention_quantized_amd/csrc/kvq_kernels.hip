@@ -764,8 +764,11 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   int blk_next = block_of(NBUF);
 
   float m_run = -INFINITY, l_run = 0.0f;
-  // per-head format: acc holds the value sum times 2^-r_run, r_run the largest V-scale exponent
-  // seen so far (keeps P' = p * s_v * 2^-r_run in [0, 2), inside f16 range, whatever the scales)
+  // per-head format: acc holds the value sum times 2^(kPvBias - r_run), r_run the largest V-scale
+  // exponent seen so far: P' = p * s_v * 2^(kPvBias - r_run) stays below 2^kPvBias (f16 range,
+  // whatever the scales), and tokens whose scale is up to about 2^kPvBias below the largest one
+  // still have P' in f16's normal range (below it hi and lo keep only absolute precision)
+  constexpr int kPvBias = 14;
   int r_run = -1000;
   f4_t acc[NT];
 #pragma unroll
@@ -877,7 +880,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     }
     const int nv = min(max(lim - 4 * q4, 0), 4);  // valid tokens among the lane's 4
     if constexpr (HEADSC) {
-      // ---- P.V, per-head format: P' = p * s_v * 2^-r_run per token (once per page), f16 hi + lo
+      // ---- P.V, per-head format: P' = p * s_v * 2^(kPvBias - r_run) per token (once per page), f16 hi + lo
       // packed along K as below.  Scales of tokens past the context are masked to 0.
       const u4_t vs4 = vsb[b];
       const uint32_t w0 = vs4[0], w1 = vs4[1], w2 = vs4[2], w3 = vs4[3];
@@ -894,7 +897,7 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       }
       float pv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pv[i] = p[i] * ldexpf(sv[i], -r_run);
+      for (int i = 0; i < 4; ++i) pv[i] = p[i] * ldexpf(sv[i], kPvBias - r_run);
       const h2_t hi01 = {(_Float16)pv[0], (_Float16)pv[1]}, hi23 = {(_Float16)pv[2], (_Float16)pv[3]};
       const h2_t lo01 = {(_Float16)(pv[0] - (float)hi01[0]), (_Float16)(pv[1] - (float)hi01[1])};
       const h2_t lo23 = {(_Float16)(pv[2] - (float)hi23[0]), (_Float16)(pv[3] - (float)hi23[1])};
@@ -958,8 +961,8 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       blk_next = block_of(k + b + NBUF + 1);
     }
   }
-  if constexpr (HEADSC) {  // back to the true value sum: acc * 2^r_run
-    const float f = ldexpf(1.0f, r_run);
+  if constexpr (HEADSC) {  // back to the true value sum: acc * 2^(r_run - kPvBias)
+    const float f = ldexpf(1.0f, r_run - kPvBias);
 #pragma unroll
     for (int jt = 0; jt < NT; ++jt) acc[jt] *= f;
   }

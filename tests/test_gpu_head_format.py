@@ -113,6 +113,23 @@ def test_fused_step_and_several_query_tokens():
                      refm[0].reshape(12, 24, 256), refm[1].reshape(12, 24), f"per-head mq ns={ns}")
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,nq", [(256, 24, 4, 8), (256, 24, 4, 23), (128, 32, 8, 40)])
+def test_four_tile_workgroups_and_prompt_sections(D, Hq, Hkv, nq):
+    """Runs of query tokens that fill 4-tile workgroups (one wave per tile, partials stored from
+    registers) and, beyond 64 / G tokens, several query chunks, on the per-head format."""
+    pair, _, bt, lens = _problem(3400 + nq, [nq, nq + 3, 300, 900], Hq, Hkv, D)
+    rng = np.random.default_rng(3401 + nq)
+    qm = _rand_bits(rng, (len(lens), nq, Hq, D), 2)
+    ref = O.decode_mq(pair.o, qm, bt, lens)
+    S = len(lens)
+    for ns in (1, 3, 0):
+        log(f"per-head mq D={D} nq={nq} splits={ns}")
+        out, lse = K.decode_mq(pair.g, bf16_dev(qm), dev(bt), dev(lens), int(lens.max()), ns)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy().reshape(S * nq, Hq, D), lse.cpu().numpy().reshape(S * nq, Hq),
+                     ref[0].reshape(S * nq, Hq, D), ref[1].reshape(S * nq, Hq), f"per-head mq D={D} nq={nq} ns={ns}")
+
+
 @pytest.mark.parametrize("cid", [2, 3])
 def test_config(cid):
     layer = W.make_layer(cid, 0)
