@@ -172,9 +172,10 @@ int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t 
  * them (INT8 caches).  Large n_q is a prompt section over the cache: half-the-memory page,
  * section "Read the prompt using a small temporary buffer": a new prompt section attends to the
  * cached keys before it and causally to itself, the parts combined with their attention weights;
- * here straight from the INT8 pages (no converted copy), the combination being the split merge.  The query tokens of sequence s are its last n_q positions L-n_q .. L-1
- * (L = context_lens[s], which includes them): query token i attends to the keys at positions
- * 0 .. L-n_q+i.  n_q == 1 is kvq_decode_attention.
+ * here straight from the INT8 pages (no converted copy), the combination being the split merge.
+ * The query tokens of sequence s are its last n_q positions L-n_q .. L-1 (L = context_lens[s],
+ * which includes them): query token i attends to the keys at positions 0 .. L-n_q+i.  n_q == 1
+ * is kvq_decode_attention.
  *   q            device, bfloat16 [num_seqs][n_q][num_q_heads][D], 16-byte aligned.
  *   out          device, fp32 [num_seqs][n_q][num_q_heads][D].
  *   lse          device, fp32 [num_seqs][n_q][num_q_heads], or NULL.
@@ -200,9 +201,10 @@ int kvq_decode_attention_mq(const kvq_cache_t *cache, const void *q, int32_t num
  * quantized to int8 once, like the cache (one fp16 scale per 32 values, codes against the stored
  * scale), and Q.K runs as integer dot products on the int8 keys (v_mfma_i32_16x16x32_i8), each
  * 32-channel group's exact int32 sum scaled by its Q and K scales.  The result is attention with
- * the quantized query: it differs from kvq_decode_attention by the query's rounding (about 1% on
- * the workloads, as the page reports for its card); off by default for that reason.  Same arguments
- * and workspace as kvq_decode_attention.
+ * the quantized query: it differs from kvq_decode_attention by the query's rounding.  The page
+ * reports 1.4-2.1% on its model; on the synthetic workloads, whose queries carry x20 outlier
+ * channels, the relative L2 difference is about 9%.  Off by default for that reason.  Same
+ * arguments and workspace as kvq_decode_attention.
  */
 int kvq_decode_attention_int8qk(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,
                                 int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
