@@ -1,0 +1,85 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the algorithmic byte counts the
+roofline divides by, and the HBM-traffic summary (counter scaling by the calibration copy, and
+the digest check that stops a summary taken on other kernels from being reported)."""
+import csv
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "single MI355X" in r.stderr and "--gpus 1" in r.stderr
+
+
+def test_algorithmic_bytes_per_layer():
+    # q8_0: per (token, KV head) 2 D code bytes + 2 (D / 32) fp16 scales; at D 256 that is 544 B
+    assert bench.algorithmic_bytes(np.array([32768]), 4, 256, "int8") == 32768 * 4 * 544 == 71303168
+    assert bench.algorithmic_bytes(np.array([512]), 4, 256, "int8") == 1114112
+    # bf16: 4 D bytes; per-head INT8: 2 D codes + two fp32 scales
+    assert bench.algorithmic_bytes(np.array([32768]), 4, 256, "bf16") == 134217728
+    assert bench.algorithmic_bytes(np.array([32768]), 4, 256, "int8_head") == 32768 * 4 * 520
+    # a batch sums its sequences; D 128 has 272 B per (token, KV head)
+    lens = np.array([2048, 8192, 16384, 32768])
+    assert bench.algorithmic_bytes(lens, 4, 256, "int8") == int(lens.sum()) * 4 * 544
+    assert bench.algorithmic_bytes(np.array([1000]), 8, 128, "int8") == 1000 * 8 * 272
+    # the long-32k workload's step: 16 layers
+    cfg = W.CONFIGS[3]
+    assert bench.algorithmic_bytes(np.array(cfg.context_lens), cfg.num_kv_heads, cfg.head_dim, "int8") * 16 == 1140850688
+
+
+def _counter_csv(path, counter, split_kib, copy_kib):
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        d = 0
+        for v in copy_kib:
+            d += 1
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": "void at::native::bitwise_not_kernel(...)",
+                        "Counter_Name": counter, "Counter_Value": v})
+        for v in split_kib:
+            d += 1
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": "void kvq::decode_split_i8_kernel<256, 4, 0, 0>(...)",
+                        "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    # FETCH_SIZE reads half the copy's bytes (factor 2), WRITE_SIZE all of them (factor 1)
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [35000.0, 34990.0, 35010.0], [copy_kib / 2] * 3)
+    _counter_csv(write, "WRITE_SIZE", [1584.0] * 3, [copy_kib] * 3)
+    out = tmp_path / "summary.md"
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(out))
+    bench.pmc_summarize(str(fetch), str(write), "cmd fetch", "cmd write")
+    rec = bench.measured_traffic()
+    assert rec is not None
+    assert rec["fetch_factor"] == 2.0 and rec["write_factor"] == 1.0
+    assert rec["fetch_bytes_per_launch"] == int(35000.0 * 1024 * 2)  # the median dispatch
+    assert rec["write_bytes_per_launch"] == 1584 * 1024
+    assert rec["traffic_bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    assert rec["algorithmic_bytes_per_launch"] == 71303168
+    assert "cmd fetch" in out.read_text() and "cmd write" in out.read_text()
+
+
+def test_traffic_summary_of_other_kernels_is_not_reported(tmp_path, monkeypatch):
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [35000.0], [copy_kib / 2])
+    _counter_csv(write, "WRITE_SIZE", [1584.0], [copy_kib])
+    out = tmp_path / "summary.md"
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(out))
+    bench.pmc_summarize(str(fetch), str(write), "a", "b")
+    assert bench.measured_traffic() is not None
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
+    assert bench.measured_traffic() is None
