@@ -92,6 +92,36 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_device(what, *tensors):
+    """Every tensor handed to the library must live in GPU memory, all on one device: a kernel
+    given a host pointer would fault.  (The library takes plain pointers and cannot tell.)"""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{what}: every tensor must be on the GPU (got one on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{what}: tensors on different devices ({dev} and {t.device})")
+
+
+def _check_outputs(what, out, out_shape, lse, lse_shape, workspace):
+    if out is not None and (out.dtype != torch.float32 or tuple(out.shape) != tuple(out_shape)
+                            or not out.is_contiguous()):
+        raise ValueError(f"{what}: out must be contiguous fp32 {list(out_shape)}")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != tuple(lse_shape)
+                            or not lse.is_contiguous()):
+        raise ValueError(f"{what}: lse must be contiguous fp32 {list(lse_shape)}")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError(f"{what}: the workspace must be contiguous")
+
+
+def _cache_planes(cache):
+    return (cache.k, cache.v, cache.k_scales, cache.v_scales)
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -166,6 +196,7 @@ def write(cache: Cache, k, v, slot_mapping, *, checked: bool = False, stream=Non
     if slot_mapping.dtype != torch.int32 or not (k.is_contiguous() and v.is_contiguous()
                                                  and slot_mapping.is_contiguous()):
         raise ValueError("contiguous bf16 k/v and int32 slot_mapping required")
+    _on_device("kvq_write", k, v, slot_mapping, *_cache_planes(cache))
     fn = lib.kvq_check_write if checked else lib.kvq_write
     _check(fn(ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(slot_mapping), T, _stream(stream)), "kvq_write")
 
@@ -195,6 +226,8 @@ def _decode_args(cache, q, block_tables, context_lens, max_context_len, num_spli
     if not (block_tables.is_contiguous() and context_lens.is_contiguous()) or block_tables.dim() != 2 \
             or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables [S][max_blocks] and context_lens [S] required")
+    _check_outputs("decode", out, (S, Hq, D), lse, (S, Hq), workspace)
+    _on_device("decode", q, block_tables, context_lens, out, lse, workspace, *_cache_planes(cache))
     ns = num_splits if num_splits else choose_num_splits(cache, S, Hq, max_context_len)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
@@ -243,6 +276,8 @@ def decode_mq(cache: Cache, q, block_tables, context_lens, max_context_len: int,
             or block_tables.shape[0] != S or context_lens.shape != (S,) \
             or not (block_tables.is_contiguous() and context_lens.is_contiguous()):
         raise ValueError("int32 block_tables [S][max_blocks] and context_lens [S] required")
+    _check_outputs("decode_mq", out, (S, nq, Hq, D), lse, (S, nq, Hq), workspace)
+    _on_device("decode_mq", q, block_tables, context_lens, out, lse, workspace, *_cache_planes(cache))
     ns = num_splits if num_splits else choose_num_splits_mq(cache, S, nq, Hq, max_context_len)
     if out is None:
         out = torch.empty((S, nq, Hq, D), dtype=torch.float32, device=q.device)
@@ -268,6 +303,7 @@ def decode_step(cache: Cache, k_new, v_new, q, block_tables, context_lens, max_c
     if tuple(k_new.shape) != (S, cache.num_kv_heads, cache.head_dim) or tuple(v_new.shape) != tuple(k_new.shape) \
             or not (k_new.is_contiguous() and v_new.is_contiguous()):
         raise ValueError(f"k_new/v_new must be contiguous [{S}][{cache.num_kv_heads}][{cache.head_dim}] bf16")
+    _on_device("decode_step", k_new, v_new, q)
     args, out, lse = _decode_args(cache, q, block_tables, context_lens, max_context_len, num_splits, out, lse,
                                   workspace, want_lse)
     fn = lib.kvq_check_decode_step if checked else lib.kvq_decode_step
@@ -279,6 +315,8 @@ def decode_partials(cache: Cache, q, block_tables, context_lens, max_context_len
                     *, stream=None) -> None:
     """First half of decode: split partials into ``workspace`` (num_splits must be explicit)."""
     S, Hq, _ = (int(x) for x in q.shape)
+    _check_outputs("decode_partials", None, (), None, (), workspace)
+    _on_device("decode_partials", q, block_tables, context_lens, workspace, *_cache_planes(cache))
     st = lib.kvq_decode_partials(ctypes.byref(cache.desc), _ptr(q), _ptr(block_tables), int(block_tables.shape[1]),
                                  _ptr(context_lens), int(max_context_len), S, Hq, int(num_splits), _ptr(workspace),
                                  int(workspace.numel() * workspace.element_size()), _stream(stream))
@@ -288,6 +326,9 @@ def decode_partials(cache: Cache, q, block_tables, context_lens, max_context_len
 def decode_merge(cache: Cache, context_lens, max_context_len: int, num_seqs: int, num_q_heads: int, num_splits: int,
                  workspace, out, lse=None, *, stream=None) -> None:
     """Second half of decode: combine the partials in ``workspace`` into out (and lse)."""
+    _check_outputs("decode_merge", out, (num_seqs, num_q_heads, cache.head_dim), lse, (num_seqs, num_q_heads),
+                   workspace)
+    _on_device("decode_merge", context_lens, workspace, out, lse)
     st = lib.kvq_decode_merge(ctypes.byref(cache.desc), _ptr(context_lens), int(max_context_len), int(num_seqs),
                               int(num_q_heads), int(num_splits), _ptr(workspace),
                               int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
