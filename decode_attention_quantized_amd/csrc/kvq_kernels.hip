@@ -980,9 +980,12 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
 // LDS and runs the decode kernel's page step on its own tile (Q.K per group and fp16 scale,
 // online softmax, P' = p * s_v as f16 hi + lo, P.V).  LDS holds two pages, so the stores of page
 // k + 1 never meet the reads of page k - 1; each thread holds a quarter or an eighth of a page in
-// registers, so NBUF pages are in flight at little register cost.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// registers, so NBUF pages are in flight at little register cost.  Two forms: 4 pages in flight
+// at 2 waves per SIMD (one chunk of query tokens, e.g. a decode of 6 to 10 tokens), and 2 pages in
+// flight with the registers capped for 3 waves per SIMD (prompt sections: many chunks, where more
+// waves per SIMD cover more of each wave's dependency chain).
+template <int D, int NBUF, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void section_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
   constexpr int NW = 4;                  // waves = row tiles
   constexpr int NG = D / kGroup;         // scale groups
@@ -992,7 +995,6 @@ void section_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
   constexpr int CPT = 2 * CH / (NW * 64);  // chunks per thread per page (K and V together)
   constexpr int SCALE_B = kPage * NG * 2;  // bytes of one scale tile
   constexpr int SDW = SCALE_B / 4;
-  constexpr int NBUF = 4;                // pages in flight
   static_assert(CPT >= 1 && (NBUF & 1) == 0, "page split and LDS double buffer");
   __shared__ __attribute__((aligned(16))) h8_t s_k[2][NG][64];     // K fragments [group][lane]
   __shared__ __attribute__((aligned(16))) u4_t s_v[2][NT][64];     // V operands [tile][lane] (codes twice)
@@ -1499,8 +1501,10 @@ template <int D, int FMT>
 static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.chunks * a.Hkv * a.row_groups * a.NS);
   const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);  // LDS merge of a tile's waves
-  if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
-    hipLaunchKernelGGL((section_i8_kernel<D>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
+  if (a.rtw == 4 && FMT == 0 && a.chunks > 1)  // q8_0 prompt sections: 3 waves per SIMD
+    hipLaunchKernelGGL((section_i8_kernel<D, 2, 3>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
+  else if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
+    hipLaunchKernelGGL((section_i8_kernel<D, 4, 2>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
   else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
   else if (a.rtw == 2)
