@@ -85,6 +85,7 @@ def prepare(cid, n_layers, dtypes, keep_host_layers):
 
     states = {d: [] for d in dtypes}
     host = []
+    fill = None
     for li in range(n_layers):
         lay, t = W.make_layer_device(cid, li)
         cfg = lay.cfg
@@ -104,6 +105,8 @@ def prepare(cid, n_layers, dtypes, keep_host_layers):
             L.out = torch.empty((lay.S, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
             L.lse = torch.empty((lay.S, cfg.num_q_heads), dtype=torch.float32, device="cuda")
             states[d].append(L)
+        if li == 0:
+            fill = (k_pre, v_pre, slot_pre)
         if li < keep_host_layers:
             host.append((lay, t["k"].view(torch.int16).cpu().numpy().view(np.uint16),
                          t["v"].view(torch.int16).cpu().numpy().view(np.uint16),
@@ -111,7 +114,40 @@ def prepare(cid, n_layers, dtypes, keep_host_layers):
         del t, k_pre, v_pre, slot_pre
         torch.cuda.synchronize()
         log(f"prepared layer {li + 1}/{n_layers}")
-    return states, host, lay
+    return states, host, lay, fill
+
+
+def fill_bytes(T, Hkv, D, dtype):
+    """Algorithmic bytes of a kv_write of T tokens: the bf16 K and V rows and the slot mapping
+    read, the cache entries written (codes and scales, or bf16 values)."""
+    written = {"int8": 2 * D + 2 * (D // 32) * 2, "bf16": 4 * D, "int8_head": 2 * D + 8}[dtype]
+    return T * Hkv * (4 * D + written) + 4 * T
+
+
+def time_fill(torch, K, states, fill, Hkv, D, steps, warmup):
+    """The bulk kv_write of a prefill (every token of the context but the step's), rewritten into
+    layer 1's cache: average launch time over HIP events on the launch stream."""
+    k_pre, v_pre, slot_pre = fill
+    T = int(slot_pre.shape[0])
+    res = {"tokens": T, "what": f"kvq_write of {T} prefill tokens x {Hkv} KV heads (K and V), one launch"}
+    for d, layers in states.items():
+        cache = layers[0].cache
+        for _ in range(max(warmup, 3)):
+            K.write(cache, k_pre, v_pre, slot_pre)
+        torch.cuda.synchronize()
+        n = max(steps, 20)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            K.write(cache, k_pre, v_pre, slot_pre)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        gbs = fill_bytes(T, Hkv, D, d) / (us * 1e-6) / 1e9
+        res[d] = {"us": round(us, 2), "GB_per_s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                  "bytes": fill_bytes(T, Hkv, D, d)}
+        log(f"kv_write fill {d}: {T} tokens, {us:.1f} us, {gbs:.0f} GB/s")
+    return res
 
 
 def make_step(K, layers, S, Hq, mcl, ns, ws, fused=True):
@@ -291,7 +327,7 @@ def pmc_workload(args):
     torch.cuda.set_device(0)
     cfg = W.CONFIGS[args.config]
     n_layers = args.layers or cfg.layers
-    states, _, lay = prepare(args.config, n_layers, ["int8"], 0)
+    states, _, lay, _ = prepare(args.config, n_layers, ["int8"], 0)
     S, Hq = lay.S, cfg.num_q_heads
     mcl = int(lay.context_lens.max())
     layers = states["int8"]
@@ -439,7 +475,7 @@ def sweep(args):
     cfg = W.CONFIGS[args.config]
     n_layers = args.layers or cfg.layers
     dtypes = ["int8"] if args.no_bf16 else ["int8", "bf16"]
-    states, _, lay = prepare(args.config, n_layers, dtypes, 0)
+    states, _, lay, _ = prepare(args.config, n_layers, dtypes, 0)
     S, Hq, Hkv, D = lay.S, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     mcl = int(lay.context_lens.max())
     flush = None
@@ -523,7 +559,7 @@ def main():
     dtypes = ["int8"] + ([] if args.no_bf16 else ["bf16"]) + ([] if args.no_head_format else ["int8_head"])
     keep = 0 if args.no_cpu_baseline else n_layers
     log(f"workload {cfg.name}: {n_layers} layers, preparing caches ({', '.join(dtypes)})")
-    states, host, lay = prepare(args.config, n_layers, dtypes, keep)
+    states, host, lay, fill = prepare(args.config, n_layers, dtypes, keep)
     S, Hq, Hkv, D = lay.S, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
     mcl = int(lay.context_lens.max())
     lens = lay.context_lens
@@ -606,6 +642,7 @@ def main():
             "decode_split_us": round(b["kern_us"], 3),
             "int8_speedup_step": round(b["ms"] / r["ms"], 3),
         }
+    out["kv_write_fill"] = time_fill(torch, K, states, fill, Hkv, D, args.steps, args.warmup)
     if not args.no_int_qk:
         out["int8_qk_variant"] = time_int_qk(torch, K, states["int8"], S, Hq, mcl, r["ns"], n_layers,
                                              args.steps, args.warmup)

@@ -104,9 +104,10 @@ __device__ __forceinline__ uint32_t q8_code(float x, float s) {
   return (uint32_t)(int)q & 0xFFu;
 }
 
-// One thread per (token, KV head, K or V, 32-channel group).
+// Few tokens (fewer than a page: the step of a decode batch): one thread per (token, KV head,
+// K or V, 32-channel group), each storing its group's codes straight into the page.
 template <int D>
-__global__ __launch_bounds__(256) void kv_write_i8_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) void kv_write_i8_rows_kernel(WriteArgs a) {
   constexpr int NG = D / kGroup;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.T * a.Hkv * 2 * NG;
@@ -161,9 +162,9 @@ __global__ __launch_bounds__(256) void kv_write_i8_kernel(WriteArgs a) {
   }
 }
 
-// BF16 cache: one thread per (token, KV head, K or V, 8-channel chunk); a scatter copy.
+// BF16 cache, few tokens: one thread per (token, KV head, K or V, 8-channel chunk); a scatter copy.
 template <int D>
-__global__ __launch_bounds__(256) void kv_write_bf16_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) void kv_write_bf16_rows_kernel(WriteArgs a) {
   constexpr int NC = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.T * a.Hkv * 2 * NC;
@@ -188,6 +189,285 @@ __global__ __launch_bounds__(256) void kv_write_bf16_kernel(WriteArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       dst[bf16_v_offset(off, c0 + e)] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+  }
+}
+
+// Token windows.  Workgroup (b, h) owns the tokens 16b .. 16b + 15 of the batch for KV head h.
+// A full page is 16 tokens t0 .. t0 + 15, consecutive in the batch, whose slots are 16p, 16p + 1,
+// ..., 16p + 15 in that order (a prefill writes its pages so).  The workgroup whose window holds
+// t0 writes such a page whole, with 16-byte stores of whole page rows; every other valid token
+// of its window is written on its own.  At most one full page starts in a window, and no token
+// lies in two: the slot of any later token of a page is not a multiple of 16.
+struct WriteWindow {
+  int page_t0;      // first token of the full page that starts in this window, or -1
+  int page_blk;     // that page's block
+  uint32_t single;  // bit t: token 16b + t has a valid slot and lies in no full page
+  int32_t slot;     // lane 16 + t: the slot of token 16b + t (broadcast below)
+};
+
+// Every wave of the workgroup takes the same decision from the same 48 slots: lane l looks at
+// token 16b - 16 + l and its successor.
+__device__ __forceinline__ WriteWindow scan_window(const WriteArgs &a, int b, int lane) {
+  const int64_t t = (int64_t)b * kPage - kPage + lane;
+  const int32_t limit = a.NB * kPage;
+  const int32_t s0 = (t >= 0 && t < a.T) ? a.slot_mapping[t] : -1;
+  const int32_t s1 = (t + 1 >= 0 && t + 1 < a.T) ? a.slot_mapping[t + 1] : -1;
+  const bool v0 = s0 >= 0 && s0 < limit;
+  const uint64_t valid = __ballot(v0);
+  const uint64_t aligned = __ballot(v0 && (s0 & (kPage - 1)) == 0);
+  const uint64_t next = __ballot(v0 && s1 == s0 + 1);
+  // bit l of run: tokens l .. l + 15 have consecutive slots (15 successor bits in a row)
+  uint64_t run = next & (next >> 1);
+  run &= run >> 2;
+  run &= run >> 4;
+  run &= run >> 7;
+  const uint64_t full = aligned & run & 0xFFFFFFFFull;  // page starts at window positions 0 .. 31
+  uint64_t cover = full;                                 // tokens that some full page holds
+  cover |= cover << 1;
+  cover |= cover << 2;
+  cover |= cover << 4;
+  cover |= cover << 8;
+  WriteWindow w;
+  const uint32_t own = (uint32_t)(full >> kPage) & 0xFFFFu;
+  w.page_t0 = -1;
+  w.page_blk = 0;
+  if (own) {
+    const int l = kPage + __builtin_ctz(own);
+    w.page_t0 = b * kPage + (l - kPage);
+    w.page_blk = __builtin_amdgcn_readlane(s0, l) >> 4;
+  }
+  w.single = (uint32_t)((valid & ~cover) >> kPage) & 0xFFFFu;
+  w.slot = s0;
+  return w;
+}
+
+// Lane (q, t) of wave i covers channels 64i + 8q .. 64i + 8q + 7 (scale group 2i) and
+// 64i + 32 + 8q .. + 7 (group 2i + 1) of token t: two 16-byte loads of the bf16 row.
+__device__ __forceinline__ void load_row_halves(const uint16_t *row, int i, int q, u4_t &xa, u4_t &xb) {
+  const u4_t *p = reinterpret_cast<const u4_t *>(row + 64 * i + 8 * q);
+  xa = p[0];
+  xb = p[4];
+}
+
+// q8_0 codes of the lane's two 8-channel pieces; the group maxima are taken over the four lanes
+// q = 0 .. 3 that share the token.  The result is the 16-byte K-page unit (group 2i's eight codes,
+// then group 2i + 1's).
+__device__ __forceinline__ u4_t quant_halves(u4_t xa, u4_t xb, _Float16 &sa, _Float16 &sb) {
+  float a[8], c[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[2 * e] = bf16_lo(xa[e]);
+    a[2 * e + 1] = bf16_hi(xa[e]);
+    c[2 * e] = bf16_lo(xb[e]);
+    c[2 * e + 1] = bf16_hi(xb[e]);
+  }
+  float ma = 0.0f, mc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ma = fmaxf(ma, fabsf(a[e]));
+    mc = fmaxf(mc, fabsf(c[e]));
+  }
+  ma = fmaxf(ma, __shfl_xor(ma, 16));
+  mc = fmaxf(mc, __shfl_xor(mc, 16));
+  ma = fmaxf(ma, __shfl_xor(ma, 32));
+  mc = fmaxf(mc, __shfl_xor(mc, 32));
+  sa = q8_scale(ma);
+  sb = q8_scale(mc);
+  const float fa = (float)sa, fc = (float)sb;
+  u4_t u = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u[e >> 2] |= q8_code(a[e], fa) << (8 * (e & 3));
+    u[2 + (e >> 2)] |= q8_code(c[e], fc) << (8 * (e & 3));
+  }
+  return u;
+}
+
+// The byte of code e of the unit (e < 8: channel 64i + 8q + e; else 64i + 32 + 8q + e - 8).
+__device__ __forceinline__ uint32_t unit_byte(u4_t u, int e) { return (u[e >> 2] >> (8 * (e & 3))) & 0xFFu; }
+
+// Per-head format: the codes of the lane's 16 channels against the row scale amax / 127, the
+// row maximum taken over the workgroup's waves (s_max: one slot per wave and token, for K and V).
+template <int NWV>
+__device__ __forceinline__ void quant_rows_head(u4_t ka, u4_t kb, u4_t va, u4_t vb, float *s_max, int i, int q,
+                                                int t, u4_t &ku, u4_t &vu, float &ks, float &vs) {
+  float x[2][16];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[0][2 * e] = bf16_lo(ka[e]);
+    x[0][2 * e + 1] = bf16_hi(ka[e]);
+    x[0][8 + 2 * e] = bf16_lo(kb[e]);
+    x[0][8 + 2 * e + 1] = bf16_hi(kb[e]);
+    x[1][2 * e] = bf16_lo(va[e]);
+    x[1][2 * e + 1] = bf16_hi(va[e]);
+    x[1][8 + 2 * e] = bf16_lo(vb[e]);
+    x[1][8 + 2 * e + 1] = bf16_hi(vb[e]);
+  }
+  float m[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m[kv] = fmaxf(m[kv], fabsf(x[kv][e]));
+    m[kv] = fmaxf(m[kv], __shfl_xor(m[kv], 16));
+    m[kv] = fmaxf(m[kv], __shfl_xor(m[kv], 32));
+  }
+  if (q == 0) {
+    s_max[i * kPage + t] = m[0];
+    s_max[(NWV + i) * kPage + t] = m[1];
+  }
+  __syncthreads();
+  float r[2];
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    r[kv] = s_max[kv * NWV * kPage + t];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) r[kv] = fmaxf(r[kv], s_max[(kv * NWV + w) * kPage + t]);
+  }
+  ks = r[0] / 127.0f;
+  vs = r[1] / 127.0f;
+  ku = u4_t{0u, 0u, 0u, 0u};
+  vu = u4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    ku[e >> 2] |= q8_code(x[0][e], ks) << (8 * (e & 3));
+    vu[e >> 2] |= q8_code(x[1][e], vs) << (8 * (e & 3));
+  }
+}
+
+// INT8 caches: blockDim D (D / 64 waves), grid (windows, KV heads).  FMT 0: q8_0 (an fp16 scale per
+// 32 values); FMT 1: one fp32 scale per (token, KV head).  V pages are staged in LDS: a token's
+// codes spread over the V page at a 4-byte stride, so a whole page is stored at once.
+template <int D, int FMT>
+__global__ __launch_bounds__(D) void kv_write_i8_kernel(WriteArgs a) {
+  constexpr int NG = D / kGroup;
+  constexpr int NWV = D / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage * D];
+  __shared__ float s_max[2][2 * NWV * kPage];  // FMT 1: row maxima, one region per path
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, i = threadIdx.x >> 6, q = lane >> 4, t = lane & 15;
+  const WriteWindow w = scan_window(a, b, lane);
+  const int64_t row_stride = (int64_t)a.Hkv * D;
+  int8_t *kc = static_cast<int8_t *>(a.kc), *vc = static_cast<int8_t *>(a.vc);
+
+  // The quantized unit pair of token `tok` and the scale stores of its lane.
+  auto quant = [&](int64_t tok, int path, u4_t &ku, u4_t &vu, uint32_t &ksb, uint32_t &vsb) {
+    u4_t ka, kb, va, vb;
+    load_row_halves(a.k + tok * row_stride + h * D, i, q, ka, kb);
+    load_row_halves(a.v + tok * row_stride + h * D, i, q, va, vb);
+    if constexpr (FMT == 0) {
+      _Float16 ksa, ksb2, vsa, vsb2;
+      ku = quant_halves(ka, kb, ksa, ksb2);
+      vu = quant_halves(va, vb, vsa, vsb2);
+      ksb = __builtin_bit_cast(uint16_t, q ? ksb2 : ksa);  // lanes q = 0, 1 store groups 2i, 2i + 1
+      vsb = __builtin_bit_cast(uint16_t, q ? vsb2 : vsa);
+    } else {
+      float ks, vs;
+      quant_rows_head<NWV>(ka, kb, va, vb, s_max[path], i, q, t, ku, vu, ks, vs);
+      ksb = __float_as_uint(ks);
+      vsb = __float_as_uint(vs);
+    }
+  };
+  auto store_scales = [&](int64_t page, int tt, uint32_t ksb, uint32_t vsb) {
+    if constexpr (FMT == 0) {
+      if (q < 2) {
+        const int64_t so = (page * NG + 2 * i + q) * kPage + tt;
+        a.ks[so] = (uint16_t)ksb;
+        a.vs[so] = (uint16_t)vsb;
+      }
+    } else {
+      if (i == 0 && q < 2) reinterpret_cast<float *>(q ? a.vs : a.ks)[page * kPage + tt] = __uint_as_float(q ? vsb : ksb);
+    }
+  };
+
+  if (w.page_t0 >= 0) {
+    const int64_t page = (int64_t)w.page_blk * a.Hkv + h;
+    u4_t ku, vu;
+    uint32_t ksb, vsb;
+    quant(w.page_t0 + t, 0, ku, vu, ksb, vsb);
+    // K unit (i, q, t) is the page's 16-byte row 64i + 16q + t = this thread's index
+    *reinterpret_cast<u4_t *>(kc + page * (kPage * D) + threadIdx.x * 16) = ku;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 64 * i + 8 * q + (e & 7) + (e >> 3) * 32;
+      s_v[i8_v_offset(t, c)] = (uint8_t)unit_byte(vu, e);
+    }
+    store_scales(page, t, ksb, vsb);
+    __syncthreads();
+    *reinterpret_cast<u4_t *>(vc + page * (kPage * D) + threadIdx.x * 16) =
+        *reinterpret_cast<const u4_t *>(s_v + threadIdx.x * 16);
+  }
+
+  if (w.single) {
+    const int64_t tok = (int64_t)b * kPage + t;
+    u4_t ku, vu;
+    uint32_t ksb, vsb;
+    quant(tok < a.T ? tok : a.T - 1, 1, ku, vu, ksb, vsb);
+    const int32_t slot = __shfl(w.slot, kPage + t);
+    if ((w.single >> t) & 1u) {
+      const int off = slot & (kPage - 1);
+      const int64_t page = (int64_t)(slot >> 4) * a.Hkv + h;
+      *reinterpret_cast<u4_t *>(kc + page * (kPage * D) + (64 * i + 16 * q + off) * 16) = ku;
+      int8_t *vd = vc + page * (kPage * D);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) vd[i8_v_offset(off, 64 * i + 8 * q + (e & 7) + (e >> 3) * 32)] = (int8_t)unit_byte(vu, e);
+      store_scales(page, off, ksb, vsb);
+    }
+  }
+}
+
+// BF16 cache: a scatter copy with the same windows.  Lane (q, t) of wave i holds the two K-page
+// rows (2i, q, t) and (2i + 1, q, t) (8 channels each); V pages are staged in LDS.
+template <int D>
+__global__ __launch_bounds__(D) void kv_write_bf16_kernel(WriteArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kPage * D];
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int lane = threadIdx.x & 63, i = threadIdx.x >> 6, q = lane >> 4, t = lane & 15;
+  const WriteWindow w = scan_window(a, b, lane);
+  const int64_t row_stride = (int64_t)a.Hkv * D;
+  uint16_t *kc = static_cast<uint16_t *>(a.kc), *vc = static_cast<uint16_t *>(a.vc);
+
+  if (w.page_t0 >= 0) {
+    const int64_t tok = w.page_t0 + t;
+    const int64_t page = (int64_t)w.page_blk * a.Hkv + h;
+    u4_t ka, kb, va, vb;
+    load_row_halves(a.k + tok * row_stride + h * D, i, q, ka, kb);
+    load_row_halves(a.v + tok * row_stride + h * D, i, q, va, vb);
+    uint16_t *kd = kc + page * (kPage * D);
+    *reinterpret_cast<u4_t *>(kd + bf16_k_offset(t, 64 * i + 8 * q)) = ka;
+    *reinterpret_cast<u4_t *>(kd + bf16_k_offset(t, 64 * i + 32 + 8 * q)) = kb;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 64 * i + 8 * q + (e & 7) + (e >> 3) * 32;
+      const uint32_t wv = e < 8 ? va[(e & 7) >> 1] : vb[(e & 7) >> 1];
+      s_v[bf16_v_offset(t, c)] = (uint16_t)((wv >> (16 * (e & 1))) & 0xFFFFu);
+    }
+    __syncthreads();
+    const u4_t *sv = reinterpret_cast<const u4_t *>(s_v);
+    u4_t *vd = reinterpret_cast<u4_t *>(vc + page * (kPage * D));
+    vd[threadIdx.x] = sv[threadIdx.x];
+    vd[threadIdx.x + D] = sv[threadIdx.x + D];
+  }
+
+  if (w.single) {
+    const int64_t tok = (int64_t)b * kPage + t;
+    const int64_t src = (tok < a.T ? tok : a.T - 1) * row_stride + h * D;
+    u4_t ka, kb, va, vb;
+    load_row_halves(a.k + src, i, q, ka, kb);
+    load_row_halves(a.v + src, i, q, va, vb);
+    const int32_t slot = __shfl(w.slot, kPage + t);
+    if ((w.single >> t) & 1u) {
+      const int off = slot & (kPage - 1);
+      const int64_t page = (int64_t)(slot >> 4) * a.Hkv + h;
+      uint16_t *kd = kc + page * (kPage * D), *vd = vc + page * (kPage * D);
+      *reinterpret_cast<u4_t *>(kd + bf16_k_offset(off, 64 * i + 8 * q)) = ka;
+      *reinterpret_cast<u4_t *>(kd + bf16_k_offset(off, 64 * i + 32 + 8 * q)) = kb;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int c = 64 * i + 8 * q + (e & 7) + (e >> 3) * 32;
+        const uint32_t wv = e < 8 ? va[(e & 7) >> 1] : vb[(e & 7) >> 1];
+        vd[bf16_v_offset(off, c)] = (uint16_t)((wv >> (16 * (e & 1))) & 0xFFFFu);
+      }
+    }
   }
 }
 
@@ -1473,21 +1753,37 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 
 hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
-  if (dtype == 2) {  // per-head INT8: one wavefront per (token, head, K or V) row, 4 rows per block
+  if (dtype == 2 && a.T < kPage) {  // per-head INT8, few tokens: one wavefront per row, 4 rows per block
     const unsigned grid = (unsigned)(((int64_t)a.T * a.Hkv * 2 + 3) / 4);
     if (a.D == 256) hipLaunchKernelGGL(kv_write_i8h_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(kv_write_i8h_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const int per = (dtype == 0 ? a.D / kGroup : a.D / 8) * 2;
-  const int64_t total = (int64_t)a.T * a.Hkv * per;
-  const unsigned grid = (unsigned)((total + 255) / 256);
+  if (dtype == 2) {
+    const dim3 grid((unsigned)((a.T + kPage - 1) / kPage), (unsigned)a.Hkv);
+    if (a.D == 256) hipLaunchKernelGGL((kv_write_i8_kernel<256, 1>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((kv_write_i8_kernel<128, 1>), grid, dim3(128), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (a.T < kPage) {  // no whole page possible: the per-group writers have the shortest latency
+    const int per = (dtype == 0 ? a.D / kGroup : a.D / 8) * 2;
+    const unsigned grid = (unsigned)(((int64_t)a.T * a.Hkv * per + 255) / 256);
+    if (dtype == 0) {
+      if (a.D == 256) hipLaunchKernelGGL(kv_write_i8_rows_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL(kv_write_i8_rows_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    } else {
+      if (a.D == 256) hipLaunchKernelGGL(kv_write_bf16_rows_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL(kv_write_bf16_rows_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((a.T + kPage - 1) / kPage), (unsigned)a.Hkv);
   if (dtype == 0) {
-    if (a.D == 256) hipLaunchKernelGGL(kv_write_i8_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(kv_write_i8_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    if (a.D == 256) hipLaunchKernelGGL((kv_write_i8_kernel<256, 0>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((kv_write_i8_kernel<128, 0>), grid, dim3(128), 0, stream, a);
   } else {
-    if (a.D == 256) hipLaunchKernelGGL(kv_write_bf16_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(kv_write_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    if (a.D == 256) hipLaunchKernelGGL(kv_write_bf16_kernel<256>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(kv_write_bf16_kernel<128>, grid, dim3(128), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -123,6 +123,11 @@ typedef struct {
  * Valid slots must be unique within one call (caller's contract; the fast path does not
  * check it).  Writing a slot replaces every code and scale of that (slot, head) row.
  * num_tokens == 0 is a no-op.  Asynchronous on `stream`.
+ * Fewer than 16 tokens (a decode batch's step) are written by one thread per 32-value group
+ * (BF16: per 8 values; per-head format: one wavefront per row).  From 16 tokens on, each
+ * workgroup takes 16 consecutive tokens of the call; a run of 16 tokens whose slots fill one
+ * page in order (as a prefill writes them) is stored as whole page rows.  Results are the same
+ * byte for byte either way.
  */
 int kvq_write(const kvq_cache_t *cache, const void *k, const void *v, const int32_t *slot_mapping,
               int32_t num_tokens, void *stream);

@@ -106,6 +106,55 @@ def test_write_random_bitexact(dtype):
         pair.assert_cache_equal()
 
 
+def _prefill_slots(rng, nb):
+    """A prefill-shaped slot map over a pool of nb blocks, in pieces with distinct blocks:
+    sequences of ragged lengths filling their pages in order (so whole pages begin at every
+    position of a 16-token window), a page whose run is broken by a skipped token, a page written
+    in reverse order, a run of 16 consecutive slots that straddles two pages, a page with an
+    out-of-pool slot in its middle, and the last block of the pool."""
+    blocks = list(rng.permutation(nb - 1))
+    take = lambda: int(blocks.pop())
+    slots = []
+    for L in (37, 16, 1, 50, 33, 18, 31, 47):
+        pages = [take() for _ in range((L + PAGE - 1) // PAGE)]
+        slots += [pages[t // PAGE] * PAGE + t % PAGE for t in range(L)]
+    b = take()
+    slots += [b * PAGE + k for k in range(PAGE) if k != 5] + [-1]
+    b = take()
+    slots += [b * PAGE + PAGE - 1 - k for k in range(PAGE)]
+    b1, b2 = take(), take()
+    slots += [b1 * PAGE + 3 + k for k in range(PAGE - 3)] + [b2 * PAGE + k for k in range(3)]
+    b = take()
+    slots += [b * PAGE + k if k != 9 else nb * PAGE + 9 for k in range(PAGE)]
+    slots += [(nb - 1) * PAGE + k for k in range(PAGE)]
+    return np.array(slots, dtype=np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["int8", "bf16", "int8_head"])
+@pytest.mark.parametrize("D", [128, 256])
+def test_write_prefill_pages_bitexact(dtype, D):
+    rng = np.random.default_rng(300 + D)
+    Hkv, nb = 3, 40
+    slots = _prefill_slots(rng, nb)
+    T = len(slots)
+    pair = Pair(dtype, nb, Hkv, D)
+    scale = np.exp2(rng.uniform(-12, 12, size=(T, Hkv, 1))).astype(np.float32)
+    k = W.f32_to_bf16_bits((rng.standard_normal((T, Hkv, D)) * scale).astype(np.float32))
+    v = W.f32_to_bf16_bits((rng.standard_normal((T, Hkv, D)) * scale).astype(np.float32))
+    log(f"write prefill pages {dtype} D={D} T={T}")
+    pair.write(k, v, slots)
+    pair.assert_cache_equal()
+    # the same rows shifted by 1 .. 15 batch positions (pages now start elsewhere in the windows)
+    for shift in (1, 7, 15):
+        pair2 = Pair(dtype, nb, Hkv, D)
+        s2 = np.concatenate([np.full(shift, -1, np.int32), slots])
+        k2 = np.concatenate([k[:shift], k])
+        v2 = np.concatenate([v[:shift], v])
+        log(f"write prefill pages {dtype} D={D} shift={shift}")
+        pair2.write(k2, v2, s2)
+        pair2.assert_cache_equal()
+
+
 @pytest.mark.parametrize("cid", [1, 2])
 @pytest.mark.parametrize("dtype", ["int8", "bf16"])
 def test_write_config_bitexact(cid, dtype):
