@@ -95,13 +95,52 @@ __device__ __forceinline__ void pin4(f4_t &v) {
 // division and a round to nearest even.
 __device__ __forceinline__ _Float16 q8_scale(float amax) { return (_Float16)fminf(amax / 127.0f, 65504.0f); }
 
-// The code of x against the stored scale s (as fp32): rint(x / s) (nearest even) clamped to
-// +-127; 0 when s is 0 or x / s is NaN.  Returned as the code's byte.
-__device__ __forceinline__ uint32_t q8_code(float x, float s) {
-  float q = __builtin_rintf(x / s);
-  q = (q != q) ? 0.0f : fminf(fmaxf(q, -127.0f), 127.0f);
-  q = (s != 0.0f) ? q : 0.0f;
-  return (uint32_t)(int)q & 0xFFu;
+// The codes of N values against the stored scale s (as fp32): rint(x / s) (nearest even) clamped
+// to +-127; 0 when s is 0 or x / s is NaN.  Packed four to a word, byte e % 4 of word e / 4.
+// x * (1 / s), with 1 / s correctly rounded, lies within 1.5 * 2^-23 |x / s| of the correctly
+// rounded quotient x / s, so for |x / s| < 256 (above that both clamp) the two round to the same
+// integer unless x * (1 / s) is within 2^-12 of a half-integer.  Only such values, and values
+// where the product is not finite (1 / s overflows for an fp32 scale below 2^-128), take the
+// quotient itself, in a block that a lane enters only when it holds one.
+template <int N>
+__device__ __forceinline__ void q8_codes(const float *x, float s, uint32_t *packed) {
+  const float rs = 1.0f / s;
+  float q[N];
+  bool near = false;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    q[e] = x[e] * rs;
+    near |= !(fabsf(__builtin_amdgcn_fractf(q[e]) - 0.5f) >= 0x1p-12f);  // NaN: not finite
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      if (!(fabsf(__builtin_amdgcn_fractf(q[e]) - 0.5f) >= 0x1p-12f)) q[e] = x[e] / s;
+  }
+#pragma unroll
+  for (int w = 0; w < N / 4; ++w) packed[w] = 0u;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    float r = __builtin_rintf(q[e]);
+    r = (r != r) ? 0.0f : fminf(fmaxf(r, -127.0f), 127.0f);
+    r = (s != 0.0f) ? r : 0.0f;
+    packed[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+  }
+}
+
+// The same codes from the quotient itself, with no branch: for the quantization inside the
+// decode kernels, whose prologue the compiler schedules as one straight block.
+template <int N>
+__device__ __forceinline__ void q8_codes_div(const float *x, float s, uint32_t *packed) {
+#pragma unroll
+  for (int w = 0; w < N / 4; ++w) packed[w] = 0u;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    float r = __builtin_rintf(x[e] / s);
+    r = (r != r) ? 0.0f : fminf(fmaxf(r, -127.0f), 127.0f);
+    r = (s != 0.0f) ? r : 0.0f;
+    packed[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+  }
 }
 
 // Few tokens (fewer than a page: the step of a decode batch): one thread per (token, KV head,
@@ -139,10 +178,7 @@ __global__ __launch_bounds__(256) void kv_write_i8_rows_kernel(WriteArgs a) {
   const _Float16 s16 = q8_scale(amax);
   const float s = (float)s16;
   uint32_t packed[kGroup / 4];
-#pragma unroll
-  for (int i = 0; i < kGroup / 4; ++i) packed[i] = 0u;
-#pragma unroll
-  for (int i = 0; i < kGroup; ++i) packed[i >> 2] |= q8_code(x[i], s) << (8 * (i & 3));
+  q8_codes<kGroup>(x, s, packed);
   const int64_t page = (int64_t)blk * a.Hkv + h;
   const uint16_t sbits = __builtin_bit_cast(uint16_t, s16);
   if (which == 0) {
@@ -273,14 +309,10 @@ __device__ __forceinline__ u4_t quant_halves(u4_t xa, u4_t xb, _Float16 &sa, _Fl
   mc = fmaxf(mc, __shfl_xor(mc, 32));
   sa = q8_scale(ma);
   sb = q8_scale(mc);
-  const float fa = (float)sa, fc = (float)sb;
-  u4_t u = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    u[e >> 2] |= q8_code(a[e], fa) << (8 * (e & 3));
-    u[2 + (e >> 2)] |= q8_code(c[e], fc) << (8 * (e & 3));
-  }
-  return u;
+  uint32_t pa[2], pc[2];
+  q8_codes<8>(a, (float)sa, pa);
+  q8_codes<8>(c, (float)sb, pc);
+  return u4_t{pa[0], pa[1], pc[0], pc[1]};
 }
 
 // The byte of code e of the unit (e < 8: channel 64i + 8q + e; else 64i + 32 + 8q + e - 8).
@@ -325,13 +357,11 @@ __device__ __forceinline__ void quant_rows_head(u4_t ka, u4_t kb, u4_t va, u4_t 
   }
   ks = r[0] / 127.0f;
   vs = r[1] / 127.0f;
-  ku = u4_t{0u, 0u, 0u, 0u};
-  vu = u4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    ku[e >> 2] |= q8_code(x[0][e], ks) << (8 * (e & 3));
-    vu[e >> 2] |= q8_code(x[1][e], vs) << (8 * (e & 3));
-  }
+  uint32_t pk[4], pv[4];
+  q8_codes<16>(x[0], ks, pk);
+  q8_codes<16>(x[1], vs, pv);
+  ku = u4_t{pk[0], pk[1], pk[2], pk[3]};
+  vu = u4_t{pv[0], pv[1], pv[2], pv[3]};
 }
 
 // INT8 caches: blockDim D (D / 64 waves), grid (windows, KV heads).  FMT 0: q8_0 (an fp16 scale per
@@ -580,7 +610,7 @@ __device__ __forceinline__ void pin_rows(u2_t &kr, u2_t &vr) {
 }
 
 // INT8 cache: the group maximum is reduced over the 8 lanes of each 32-channel group; scale and
-// codes follow the same arithmetic as kv_write (q8_scale, q8_code), so the bytes are identical.
+// codes follow the same arithmetic as kv_write (q8_scale, q8_codes), so the bytes are identical.
 template <int D>
 __device__ __forceinline__ void write_new_i8(const DecodeArgs &a, int64_t page, int t, u2_t kr, u2_t vr, int lane) {
   constexpr int NG = D / kGroup;
@@ -598,9 +628,8 @@ __device__ __forceinline__ void write_new_i8(const DecodeArgs &a, int64_t page, 
     amax = fmaxf(amax, __shfl_xor(amax, 4));
     const _Float16 s16 = q8_scale(amax);
     const float sc = (float)s16;
-    uint32_t codes = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) codes |= q8_code(x[i], sc) << (8 * i);
+    uint32_t codes;
+    q8_codes_div<4>(x, sc, &codes);
     if (c0 < D) {
       int8_t *dst = static_cast<int8_t *>(const_cast<void *>(which ? a.vc : a.kc)) + page * (kPage * D);
       if (which == 0) {
@@ -617,8 +646,10 @@ __device__ __forceinline__ void write_new_i8(const DecodeArgs &a, int64_t page, 
 }
 
 // Per-head INT8 format: one fp32 scale per (token, head) row.  The row's maximum is reduced over
-// the whole wavefront; the scale is amax / 127 (fp32 division), the codes q8_code(x, scale).
+// the whole wavefront; the scale is amax / 127 (fp32 division), the codes q8_codes(x, scale).
 // Returns this lane's 4 codes (one byte each, channels 4 lane .. 4 lane + 3) and the scale.
+// BRANCHLESS: the division form (inside the decode kernels).
+template <bool BRANCHLESS>
 __device__ __forceinline__ uint32_t quant_row_head(uint32_t w0, uint32_t w1, float &scale) {
   const float x[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
   float amax = 0.0f;
@@ -627,9 +658,9 @@ __device__ __forceinline__ uint32_t quant_row_head(uint32_t w0, uint32_t w1, flo
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
   scale = amax / 127.0f;
-  uint32_t codes = 0u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) codes |= q8_code(x[i], scale) << (8 * i);
+  uint32_t codes;
+  if constexpr (BRANCHLESS) q8_codes_div<4>(x, scale, &codes);
+  else q8_codes<4>(x, scale, &codes);
   return codes;
 }
 
@@ -657,7 +688,7 @@ __device__ __forceinline__ void write_new_i8h(const DecodeArgs &a, int64_t page,
   for (int which = 0; which < 2; ++which) {
     const uint32_t w0 = which ? vr[0] : kr[0], w1 = which ? vr[1] : kr[1];
     float scale;
-    const uint32_t codes = quant_row_head(w0, w1, scale);
+    const uint32_t codes = quant_row_head<true>(w0, w1, scale);
     int8_t *dst = static_cast<int8_t *>(const_cast<void *>(which ? a.vc : a.kc)) + page * (kPage * D);
     float *sc = reinterpret_cast<float *>(const_cast<uint16_t *>(which ? a.vs : a.ks)) + page * kPage;
     store_row_head<D>(dst, sc, which, t, lane, codes, scale);
@@ -681,7 +712,7 @@ __global__ __launch_bounds__(256) void kv_write_i8h_kernel(WriteArgs a) {
   const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(src), 0, D * 2, 0x00020000);
   const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(r, lane * 8, 0, 0));
   float scale;
-  const uint32_t codes = quant_row_head(w[0], w[1], scale);
+  const uint32_t codes = quant_row_head<false>(w[0], w[1], scale);
   const int64_t page = (int64_t)blk * a.Hkv + h;
   int8_t *dst = static_cast<int8_t *>(which ? a.vc : a.kc) + page * (kPage * D);
   float *sc = reinterpret_cast<float *>(which ? a.vs : a.ks) + page * kPage;
@@ -1042,12 +1073,9 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
       amax = rows_max(amax);  // the group's 32 values sit in the 4 lanes of the row
       const float sc16 = (float)q8_scale(amax);
-      uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo |= q8_code(x[e], sc16) << (8 * e);
-        hi |= q8_code(x[4 + e], sc16) << (8 * e);
-      }
+      uint32_t lohi[2];
+      q8_codes_div<8>(x, sc16, lohi);
+      const uint32_t lo = lohi[0], hi = lohi[1];
       qi[g] = ((uint64_t)hi << 32) | lo;
       sq[g] = sc16;
     }

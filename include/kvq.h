@@ -39,8 +39,8 @@
  *
  * Arithmetic.  kvq_write: x = float(bf16); amax = max |x| over 32 consecutive channels of one
  * (token, KV head); d = amax / 127 (IEEE fp32 division); s = fp16(min(d, 65504)), round to
- * nearest even, stored; code = clamp(rint(x / s), -127, 127) in fp32 with ties to even,
- * 0 when s == 0.  The decoded value is code * s.  kvq_decode_attention returns, per sequence s
+ * nearest even, stored; code = clamp(rint(x / s), -127, 127) in fp32 with ties to even
+ * (x / s the correctly rounded quotient), 0 when s == 0.  The decoded value is code * s.  kvq_decode_attention returns, per sequence s
  * and query head hq (KV head h = hq / (Hq / Hkv)):
  *   out[s][hq][:] = sum_t softmax_t(q . k_t / sqrt(D)) v_t   over t < context_lens[s]
  *   lse[s][hq]    = ln sum_t exp(q . k_t / sqrt(D))            (natural log)

@@ -155,6 +155,56 @@ def test_write_prefill_pages_bitexact(dtype, D):
         pair2.assert_cache_equal()
 
 
+def _near_tie_rows(rng, T, Hkv, D, per_head):
+    """bf16 rows whose quotients x / s by their own stored scale are exact half-integers (ties, to
+    even) or lie within 2^-10 of one, so that the rounding decision is as close as it gets.  The
+    scale follows the quantizer's rule from the row's (or 32-group's) maximum: fp32 amax / 127,
+    then (q8_0) binary16 round to nearest even."""
+    glen = D if per_head else 32
+    out = np.zeros((T, Hkv, D), np.float32)
+    for t in range(T):
+        for h in range(Hkv):
+            for g0 in range(0, D, glen):
+                e = int(rng.integers(-12, 12))
+                if rng.random() < 0.3:   # power-of-two scale: amax 127 * 2^e, exact ties (n + 1/2) 2^e
+                    n = rng.integers(-127, 127, size=glen)
+                    vals = (n + 0.5) * 2.0 ** e
+                    vals[0] = 127 * 2.0 ** e
+                else:
+                    amax = float(W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.array([rng.uniform(20, 127) * 2.0 ** e], np.float32)))[0])
+                    d = np.float32(amax) / np.float32(127)
+                    sc = np.float32(d) if per_head else np.float32(np.float16(min(d, 65504)))
+                    cand = W.bf16_bits_to_f32(W.f32_to_bf16_bits(
+                        rng.uniform(-amax, amax, size=16384).astype(np.float32)))
+                    qt = cand / sc                                    # IEEE float32 division
+                    fr = np.abs((qt - np.floor(qt)) - 0.5)
+                    pick = cand[np.argsort(fr)[:glen]]
+                    vals = np.concatenate([[amax], pick[:glen - 1]])
+                out[t, h, g0:g0 + glen] = rng.permutation(vals)
+    return W.f32_to_bf16_bits(out)
+
+
+@pytest.mark.parametrize("dtype", ["int8", "int8_head"])
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("T", [8, 64])
+def test_write_rounding_ties_bitexact(dtype, D, T):
+    """Codes at and next to rounding ties, through both writers (fewer than 16 tokens, and the
+    16-token windows), against the oracle byte for byte."""
+    rng = np.random.default_rng(500 + D + T)
+    Hkv = 2
+    nb = (T + PAGE - 1) // PAGE + 2
+    k = _near_tie_rows(rng, T, Hkv, D, dtype == "int8_head")
+    v = _near_tie_rows(rng, T, Hkv, D, dtype == "int8_head")
+    slots = np.arange(T, dtype=np.int32) + PAGE  # whole pages from block 1 on (the windows' page path)
+    pair = Pair(dtype, nb, Hkv, D)
+    log(f"write rounding ties {dtype} D={D} T={T}")
+    pair.write(k, v, slots)
+    pair.assert_cache_equal()
+    pair2 = Pair(dtype, nb, Hkv, D)
+    pair2.write(k, v, rng.permutation(nb * PAGE)[:T].astype(np.int32))  # scattered: per-token stores
+    pair2.assert_cache_equal()
+
+
 @pytest.mark.parametrize("cid", [1, 2])
 @pytest.mark.parametrize("dtype", ["int8", "bf16"])
 def test_write_config_bitexact(cid, dtype):
