@@ -37,6 +37,16 @@ def test_algorithmic_bytes_per_layer():
     assert bench.algorithmic_bytes(np.array(cfg.context_lens), cfg.num_kv_heads, cfg.head_dim, "int8") * 16 == 1140850688
 
 
+def test_fill_bytes():
+    # a prefill kv_write reads 2 bf16 rows (K, V) of D values and the slot, and writes the entries:
+    # q8_0 codes 2 D + scales 2 (D / 32) fp16 = 544 B at D 256; BF16 4 D; per-head 2 D + 2 fp32
+    T = 32767
+    assert bench.fill_bytes(T, 4, 256, "int8") == T * 4 * (1024 + 544) + 4 * T == 205645692
+    assert bench.fill_bytes(T, 4, 256, "bf16") == T * 4 * (1024 + 1024) + 4 * T
+    assert bench.fill_bytes(T, 4, 256, "int8_head") == T * 4 * (1024 + 520) + 4 * T
+    assert bench.fill_bytes(10, 8, 128, "int8") == 10 * 8 * (512 + 272) + 40
+
+
 def _counter_csv(path, counter, split_kib, copy_kib):
     fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     with open(path, "w", newline="") as f:
