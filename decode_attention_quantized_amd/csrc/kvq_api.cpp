@@ -17,6 +17,8 @@ namespace {
 constexpr int kMaxSplits = 4096;
 constexpr int kMaxGqa = 16;
 
+constexpr int32_t kMaxKvHeads = 65535;
+
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int check_cache(const kvq_cache_t *c) {
@@ -25,6 +27,7 @@ int check_cache(const kvq_cache_t *c) {
   if (c->block_size != kvq::kPage) return KVQ_ERR_UNSUPPORTED;
   if (c->head_dim != 128 && c->head_dim != 256) return KVQ_ERR_UNSUPPORTED;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return KVQ_ERR_INVALID_ARG;
+  if (c->num_kv_heads > kMaxKvHeads) return KVQ_ERR_UNSUPPORTED;  // the writers' grid has a row per KV head
   if ((int64_t)c->num_blocks * kvq::kPage > INT32_MAX) return KVQ_ERR_INVALID_ARG;
   if (!c->k || !c->v || !aligned(c->k, 256) || !aligned(c->v, 256)) return KVQ_ERR_INVALID_ARG;
   if (c->dtype != KVQ_BF16) {

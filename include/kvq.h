@@ -110,7 +110,7 @@ typedef struct {
   int32_t dtype;        /* kvq_dtype_t */
   int32_t num_blocks;   /* pages per KV head in the pool */
   int32_t block_size;   /* tokens per page; must be 16 */
-  int32_t num_kv_heads; /* Hkv */
+  int32_t num_kv_heads; /* Hkv: 1 .. 65535 */
   int32_t head_dim;     /* D: 128 or 256 */
   void *k, *v;          /* code / value planes (layout above) */
   void *k_scales, *v_scales; /* scale planes: binary16 (q8_0) or fp32 (per head); NULL for BF16 */

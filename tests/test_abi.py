@@ -81,6 +81,7 @@ def test_write_rejects_invalid_arguments():
     assert _write(_desc(dtype=3)) == -2
     assert _write(_desc(nb=0)) == -1
     assert _write(_desc(hkv=0)) == -1
+    assert _write(_desc(hkv=65536)) == -2              # more KV heads than the writers' grid has rows
     assert _write(_desc(k=None)) == -1
     assert _write(_desc(k=FAKE + 16)) == -1            # plane base not 256-aligned
     assert _write(_desc(ks=None)) == -1                # INT8 needs scale planes
