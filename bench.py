@@ -289,6 +289,7 @@ def time_split_kernel(torch, K, layers, mcl, ns, ws, passes):
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_i8_long32k_hbm_traffic.md")
+FILL_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kv_write_i8_long32k_fill_hbm_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_kernels.hip")
 
 
@@ -298,11 +299,11 @@ def kernel_source_digest():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per decode_split launch from the committed counter summary, or None when that
-    summary is missing or was taken on a different kernel source."""
+def measured_traffic(path=None):
+    """HBM bytes per launch from a committed counter summary (the decode_split one by default),
+    or None when that summary is missing or was taken on a different kernel source."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(path or TRAFFIC_SUMMARY) as f:
             for line in f:
                 if line.startswith("{"):
                     rec = json.loads(line)
@@ -317,8 +318,9 @@ COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes
 
 
 def pmc_workload(args):
-    """Runs what the HBM-traffic counters are taken on: a plain copy kernel of known size (the
-    calibration), then the decode_split launches of every layer, a few times each."""
+    """Runs what the HBM-traffic counters are taken on: the prefill fill of every layer's cache
+    (one kvq_write each, at set-up), a plain copy kernel of known size (the calibration), then
+    the decode_split launches of every layer, a few times each."""
     import torch
 
     import decode_attention_quantized_amd as K
@@ -345,42 +347,44 @@ def pmc_workload(args):
     log(f"pmc workload done: splits {ns}")
 
 
-def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
-    """Turns the two counter runs of pmc_workload into the traffic summary bench.py reads."""
+def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, algorithmic, title, path):
+    """Per-dispatch medians of FETCH_SIZE and WRITE_SIZE for the kernels whose name holds `tag`,
+    scaled by what the same counters read for the calibration copy; written to `path`."""
     import csv
 
-    def per_dispatch(path, counter):
-        split, copy = [], []
-        with open(path) as f:
+    def per_dispatch(path_, counter):
+        mine, copy = [], []
+        with open(path_) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
                 v = float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
-                if "decode_split_i8_kernel" in r["Kernel_Name"]:
-                    split.append(v)
+                if tag in r["Kernel_Name"]:
+                    mine.append(v)
                 elif "bitwise_not" in r["Kernel_Name"]:
                     copy.append(v)
-        return float(np.median(split)), float(np.median(copy)), len(split), len(copy)
+        med = lambda x: float(np.median(x)) if x else 0.0
+        return med(mine), med(copy), len(mine), len(copy)
 
     fs, fc, nfs, nfc = per_dispatch(fetch_csv, "FETCH_SIZE")
     ws_, wc, nws, nwc = per_dispatch(write_csv, "WRITE_SIZE")
+    if min(nfs, nws, nfc, nwc) == 0:
+        log(f"no {tag} or calibration dispatches in the counter runs: {os.path.relpath(path, ROOT)} not written")
+        return None
     kf, kw = COPY_BYTES / fc, COPY_BYTES / wc
-    import workloads as W
-    cfg = W.CONFIGS[3]
-    layer_bytes = algorithmic_bytes(np.array(cfg.context_lens), cfg.num_kv_heads, cfg.head_dim, "int8")
     rec = {
-        "kernel": "decode_split_i8_kernel<256, 4, 0, 0>",
+        "kernel": kernel,
         "workload": "long-32k layer: batch 1, context 32768, 24/4 heads, head_dim 256",
         "kernel_source_sha256": kernel_source_digest(),
         "fetch_kib_per_launch_raw": round(fs / 1024, 1), "write_kib_per_launch_raw": round(ws_ / 1024, 1),
         "copy_fetch_kib_raw": round(fc / 1024, 1), "copy_write_kib_raw": round(wc / 1024, 1),
         "copy_bytes": COPY_BYTES, "fetch_factor": round(kf, 4), "write_factor": round(kw, 4),
         "fetch_bytes_per_launch": int(fs * kf), "write_bytes_per_launch": int(ws_ * kw),
-        "traffic_bytes_per_launch": int(fs * kf + ws_ * kw), "algorithmic_bytes_per_launch": layer_bytes,
-        "dispatches": {"split_fetch": nfs, "split_write": nws, "copy_fetch": nfc, "copy_write": nwc},
+        "traffic_bytes_per_launch": int(fs * kf + ws_ * kw), "algorithmic_bytes_per_launch": algorithmic,
+        "dispatches": {"kernel_fetch": nfs, "kernel_write": nws, "copy_fetch": nfc, "copy_write": nwc},
     }
     text = [
-        "# HBM traffic: decode_split_i8_kernel<256, 4, 0, 0> (q8_0), long-32k layer (context 32768, 24/4 heads, D 256)",
+        title,
         "",
         "Two counter runs of the same program, one counter each (commands from the repository root",
         "on one MI355X; `$REPO` is the repository root):",
@@ -392,21 +396,40 @@ def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
         "",
         "| | raw KiB | factor | bytes |",
         "|---|---|---|---|",
-        f"| split FETCH_SIZE | {fs / 1024:.1f} | {kf:.4f} | {int(fs * kf)} |",
-        f"| split WRITE_SIZE | {ws_ / 1024:.1f} | {kw:.4f} | {int(ws_ * kw)} |",
+        f"| kernel FETCH_SIZE | {fs / 1024:.1f} | {kf:.4f} | {int(fs * kf)} |",
+        f"| kernel WRITE_SIZE | {ws_ / 1024:.1f} | {kw:.4f} | {int(ws_ * kw)} |",
         f"| copy FETCH_SIZE | {fc / 1024:.1f} | | {COPY_BYTES} |",
         f"| copy WRITE_SIZE | {wc / 1024:.1f} | | {COPY_BYTES} |",
         "",
-        f"Algorithmic bytes per launch: {layer_bytes}; measured / algorithmic = "
-        f"{(fs * kf + ws_ * kw) / layer_bytes:.3f}.  The record below is what bench.py reads (it reports",
+        f"Algorithmic bytes per launch: {algorithmic}; measured / algorithmic = "
+        f"{(fs * kf + ws_ * kw) / algorithmic:.3f}.  The record below is what bench.py reads (it reports",
         "it only while the kernel source still has the digest it was taken on):",
         "",
         json.dumps(rec),
         "",
     ]
-    with open(TRAFFIC_SUMMARY, "w") as f:
+    with open(path, "w") as f:
         f.write("\n".join(text))
     print("\n".join(text))
+    return rec
+
+
+def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
+    """Turns the two counter runs of pmc_workload into the traffic summaries bench.py reads: the
+    decode_split launches, and the prefill fill's kvq_write launches (one 32767-token write per
+    layer at set-up)."""
+    import workloads as W
+    cfg = W.CONFIGS[3]
+    lens = np.array(cfg.context_lens)
+    _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, "decode_split_i8_kernel<256, 4, 0, 0>",
+                     "decode_split_i8_kernel", algorithmic_bytes(lens, cfg.num_kv_heads, cfg.head_dim, "int8"),
+                     "# HBM traffic: decode_split_i8_kernel<256, 4, 0, 0> (q8_0), long-32k layer (context 32768, "
+                     "24/4 heads, D 256)", TRAFFIC_SUMMARY)
+    T = int(lens[0]) - 1
+    _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, "kv_write_i8_kernel<256, 0>",
+                     "kv_write_i8_kernel<256, 0>", fill_bytes(T, cfg.num_kv_heads, cfg.head_dim, "int8"),
+                     f"# HBM traffic: kv_write_i8_kernel<256, 0> (q8_0), prefill fill of a long-32k layer ({T} tokens, "
+                     "4 KV heads, D 256)", FILL_TRAFFIC_SUMMARY)
 
 
 def cpu_baseline(host, states_int8, budget_s):
@@ -643,6 +666,10 @@ def main():
             "int8_speedup_step": round(b["ms"] / r["ms"], 3),
         }
     out["kv_write_fill"] = time_fill(torch, K, states, fill, Hkv, D, args.steps, args.warmup)
+    ftr = measured_traffic(FILL_TRAFFIC_SUMMARY) if (args.config == 3 and D == 256) else None
+    if ftr is not None and "int8" in out["kv_write_fill"]:
+        out["kv_write_fill"]["int8"]["traffic"] = ftr["traffic_bytes_per_launch"]
+        out["kv_write_fill"]["int8"]["traffic_source"] = os.path.relpath(FILL_TRAFFIC_SUMMARY, ROOT)
     if not args.no_int_qk:
         out["int8_qk_variant"] = time_int_qk(torch, K, states["int8"], S, Hq, mcl, r["ns"], n_layers,
                                              args.steps, args.warmup)

@@ -47,12 +47,16 @@ def test_fill_bytes():
     assert bench.fill_bytes(10, 8, 128, "int8") == 10 * 8 * (512 + 272) + 40
 
 
-def _counter_csv(path, counter, split_kib, copy_kib):
+def _counter_csv(path, counter, split_kib, copy_kib, fill_kib=()):
     fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=fields)
         w.writeheader()
         d = 0
+        for v in fill_kib:
+            d += 1
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": "void kvq::kv_write_i8_kernel<256, 0>(kvq::WriteArgs)",
+                        "Counter_Name": counter, "Counter_Value": v})
         for v in copy_kib:
             d += 1
             w.writerow({"Dispatch_Id": d, "Kernel_Name": "void at::native::bitwise_not_kernel(...)",
@@ -71,6 +75,7 @@ def test_traffic_summary_scales_by_the_calibration_copy(tmp_path, monkeypatch):
     _counter_csv(write, "WRITE_SIZE", [1584.0] * 3, [copy_kib] * 3)
     out = tmp_path / "summary.md"
     monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(out))
+    monkeypatch.setattr(bench, "FILL_TRAFFIC_SUMMARY", str(tmp_path / "fill.md"))
     bench.pmc_summarize(str(fetch), str(write), "cmd fetch", "cmd write")
     rec = bench.measured_traffic()
     assert rec is not None
@@ -89,7 +94,26 @@ def test_traffic_summary_of_other_kernels_is_not_reported(tmp_path, monkeypatch)
     _counter_csv(write, "WRITE_SIZE", [1584.0], [copy_kib])
     out = tmp_path / "summary.md"
     monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(out))
+    monkeypatch.setattr(bench, "FILL_TRAFFIC_SUMMARY", str(tmp_path / "fill.md"))
     bench.pmc_summarize(str(fetch), str(write), "a", "b")
     assert bench.measured_traffic() is not None
     monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
     assert bench.measured_traffic() is None
+
+
+def test_fill_traffic_summary(tmp_path, monkeypatch):
+    # the prefill fill's kvq_write dispatches in the same counter runs get a record of their own
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [35000.0], [copy_kib / 2], fill_kib=[67000.0, 67200.0, 67100.0])
+    _counter_csv(write, "WRITE_SIZE", [1584.0], [copy_kib], fill_kib=[69600.0] * 3)
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "split.md"))
+    monkeypatch.setattr(bench, "FILL_TRAFFIC_SUMMARY", str(tmp_path / "fill.md"))
+    bench.pmc_summarize(str(fetch), str(write), "a", "b")
+    rec = bench.measured_traffic(str(tmp_path / "fill.md"))
+    assert rec["kernel"] == "kv_write_i8_kernel<256, 0>"
+    assert rec["fetch_bytes_per_launch"] == int(67100.0 * 1024 * 2)
+    assert rec["write_bytes_per_launch"] == 69600 * 1024
+    assert rec["algorithmic_bytes_per_launch"] == bench.fill_bytes(32767, 4, 256, "int8")
+    # the decode_split record is unaffected by the writer's dispatches
+    assert bench.measured_traffic()["fetch_bytes_per_launch"] == int(35000.0 * 1024 * 2)
