@@ -897,6 +897,13 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
   }
 }
 
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt at their maxima: no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---- INT8 cache: 1-page units in a ring of register buffers, f16 MFMA for both products
 //
 // A wave owns pages p0 + wave + k * NW (k = 0, 1, ...) of its split (several query tokens with
@@ -906,7 +913,8 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
 // before anything else; the other buffers fill once Q has arrived.
 template <int D, int NW, int MQR, int FMT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
+void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables,
+                            const int32_t *__restrict__ context_lens) {
   constexpr bool MQ = MQR > 0;        // several query tokens: rows are (query token, head) pairs
   constexpr int RTW = MQ ? MQR : 1;   // row tiles per workgroup (MQ)
   constexpr int NWP = NW / RTW;       // waves that split the pages of one row tile
@@ -927,7 +935,6 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];              // rescale factors, per head
   extern __shared__ float s_merge[];                                          // [NW][G*D + 32] (dynamic)
 
-  const int32_t *__restrict__ context_lens = a.context_lens;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: keeps page math scalar
   const int rl = wave % RTW, pw = wave / RTW;  // row tile within the workgroup, page-wave index
@@ -944,21 +951,42 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   const int s = blockIdx.x / (a.NS * (MQ ? a.row_groups * a.chunks : 1) * a.Hkv);
   const int c0 = c * (MQ ? a.qchunk : 1);
   const int n_here = MQ ? min(a.qchunk, a.nq - c0) : 1;
-  const int L_full = max(0, min(context_lens[s], a.max_context_len));
-  const int L = MQ ? max(0, L_full - a.nq + c0 + n_here) : L_full;
-  const int P = (L + kPage - 1) / kPage;
   const int p0 = j * a.cpp;
-  const int p1 = min(p0 + a.cpp, P);
-  if (p0 >= p1) return;  // empty split: nothing written, the merge skips it
-  const int n_units = p1 - p0;
-
   const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
   const int voff = lane * 16;  // byte offset of this lane's 16-byte fragment in each KiB of a page
 
   // Block id of page k of the wave: a scalar load (the block table is only read here), issued
-  // one page ahead of its use so that its latency hides behind a page's work.
-  auto block_of = [&](int k) -> int { return btrow[min(p0 + pw + k * NWP, p1 - 1)]; };
+  // one page ahead of its use so that its latency hides behind a page's work.  The index is
+  // clamped to the table row, not to the context, so the first ids are requested together with
+  // the context length (one round trip before the first page request, not two); ids of pages past
+  // the split are never used to read memory (their loads have size-0 resources).
+  auto block_of = [&](int k) -> int { return btrow[min(p0 + pw + k * NWP, a.max_blocks - 1)]; };
   auto page_of = [&](int blk) -> int64_t { return (int64_t)min(max(blk, 0), a.NB - 1) * a.Hkv + h; };
+  int blk[NBUF];
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) blk[b] = block_of(b);
+  // Q and the step's new token (every wave requests the token's rows; the owning wave, known once
+  // the length has arrived, writes it) are requested in the same round trip.
+  u4_t qraw[NG];
+  if constexpr (MQ) load_q_mq<D>(a, s, h, rt, c0, n_here, n16, q4, qraw);
+  else load_q<D>(a, s, h, n16, q4, qraw);
+  u2_t knew, vnew;
+  load_new_rows<D>(a, s, h, !MQ && a.k_new != nullptr, lane, knew, vnew);
+
+  const int L_raw = context_lens[s];
+  const int L_full = max(0, min(L_raw, a.max_context_len));
+  const int L = MQ ? max(0, L_full - a.nq + c0 + n_here) : L_full;
+  const int P = (L + kPage - 1) / kPage;
+  const int p1 = min(p0 + a.cpp, P);
+  if (p0 >= p1) {  // empty split: nothing written, the merge skips it
+    // The prologue's loads and the arguments the page requests need are used on this path too, so
+    // the compiler issues them all before the branch (one round trip before the first page
+    // request) instead of sinking them into the other path behind further waits.
+    asm volatile("" ::"s"(blk[0]), "s"(blk[NBUF - 1]), "s"(a.kc), "s"(a.vc), "s"(a.ks), "s"(a.vs), "s"(a.NB),
+                 "v"(qraw[0][0]), "v"(knew[0]));
+    return;
+  }
+  const int n_units = p1 - p0;
 
   // ---- register buffers: K / V codes and the page's K / V scale tiles (one dword per lane).
   // Past the end of the split the resources have size 0: the loads return zeros without
@@ -990,23 +1018,19 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     vsb[b] = load_scales(a.vs, page, ok);
   };
 
-  int blk[NBUF];
-#pragma unroll
-  for (int b = 0; b < NBUF; ++b) blk[b] = block_of(b);
-  // The wave that holds the sequence's last page writes the step's new token into it first (its
-  // local page index k_last; written before that page is requested).
-  const int blk_last = btrow[P - 1];
-  const bool own_new =
-      !MQ && a.k_new != nullptr && p1 == P && wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
+  // The wave that holds the sequence's last page writes the step's new token into it (its local
+  // page index k_last) before it requests that page.  A length above max_context_len (outside the
+  // contract) writes nothing.  Ordering: vmcnt counts this wave's stores until the memory system
+  // has acknowledged them (then a later load of the same bytes, which misses the write-through L1,
+  // reads them back), and it retires in issue order; so before requesting page k_last the owner
+  // waits until at most the loads issued after its stores are outstanding (see wait_stores).
+  bool own_new = !MQ && a.k_new != nullptr && L_raw <= a.max_context_len && p1 == P && wave == (n_units - 1) % NW;
+  const int blk_last = own_new ? btrow[P - 1] : 0;  // (only the owner waits for it)
+  own_new = own_new && blk_last >= 0 && blk_last < a.NB;
   const int k_last = (n_units - 1) / NWP;
   // MQ: the lane's row sees keys 0 .. L - nq + token (causal among the query tokens)
   int L_row = L;
   if constexpr (MQ) L_row = L_full - a.nq + c0 + (16 * rt + n16) / a.G + 1;
-  u4_t qraw[NG];
-  if constexpr (MQ) load_q_mq<D>(a, s, h, rt, c0, n_here, n16, q4, qraw);
-  else load_q<D>(a, s, h, n16, q4, qraw);
-  u2_t knew, vnew;
-  load_new_rows<D>(a, s, h, own_new, lane, knew, vnew);
   __builtin_amdgcn_sched_barrier(0);
   const int64_t page_new = (int64_t)blk_last * a.Hkv + h;
   const int t_new = (L - 1) & (kPage - 1);
@@ -1014,7 +1038,10 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
     if constexpr (HEADSC) write_new_i8h<D>(a, page_new, t_new, knew, vnew, lane);
     else write_new_i8<D>(a, page_new, t_new, knew, vnew, lane);
   };
-  if (own_new && k_last == 0) write_new();
+  if (own_new && k_last == 0) {
+    write_new();
+    wait_vmcnt<0>();  // the stores are the youngest memory operations
+  }
   issue_k(0, 0, blk[0]);
   __builtin_amdgcn_sched_barrier(0);
   issue_v(0, 0, blk[0]);
@@ -1080,7 +1107,10 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
       sq[g] = sc16;
     }
   }
-  if (own_new && k_last != 0) write_new();
+  if (own_new && k_last != 0) {
+    write_new();
+    if (k_last < NBUF) wait_vmcnt<0>();  // page k_last is requested right below
+  }
 #pragma unroll
   for (int b = 1; b < NBUF; ++b) {
     issue_k(b, b, blk[b]);
@@ -1277,10 +1307,15 @@ void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tabl
   // A uniform trip count and no early exit: pages past the split's end read zeros and are
   // fully masked (p = 0), which keeps the in-flight buffers in fixed registers across the loop.
   const int my_units = pw < n_units ? (n_units - pw + NWP - 1) / NWP : 0;
+  // Loads per page (K and V codes, K and V scale tiles).  When page k_last (>= NBUF) is about to be
+  // requested, only the NBUF - 1 pages requested after it may still be outstanding: everything
+  // older, the owner's stores included (they were issued before page 1), has completed.
+  constexpr int kPageLoads = 2 * (NL + 1);
   for (int k = 0; k < my_units; k += NBUF) {
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
       process(b, k + b);
+      if (own_new && k + b + NBUF == k_last) wait_vmcnt<kPageLoads * (NBUF - 1)>();
       issue_k(b, k + b + NBUF, blk_next);
       issue_v(b, k + b + NBUF, blk_next);
       __builtin_amdgcn_sched_barrier(0);
@@ -1345,8 +1380,8 @@ void section_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
   if (p0 >= p1) return;  // empty split (uniform): nothing written, the merge skips it
   const int n_units = p1 - p0;
   const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
-  auto page_of = [&](int k) -> int64_t {
-    const int blk = btrow[min(p0 + k, p1 - 1)];
+  auto page_of = [&](int k) -> int64_t {  // (pages past the split are read with size-0 resources)
+    const int blk = btrow[min(p0 + k, a.max_blocks - 1)];
     return (int64_t)min(max(blk, 0), a.NB - 1) * a.Hkv + h;
   };
 
@@ -1569,24 +1604,29 @@ void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_ta
   const int j = blockIdx.x % a.NS;
   const int h = (blockIdx.x / a.NS) % a.Hkv;
   const int s = blockIdx.x / (a.NS * a.Hkv);
+  const int p0 = j * a.cpp;
+  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
+  // the block id of the wave's first page, Q and the new token's rows are requested together with
+  // the context length (the id's index is clamped to the table row, not to the context)
+  const int blk0 = btrow[min(p0 + wave, a.max_blocks - 1)];
+  u4_t qraw[NG];
+  load_q<D>(a, s, h, n16, q4, qraw);
+  u2_t knew, vnew;
+  load_new_rows<D>(a, s, h, a.k_new != nullptr, lane, knew, vnew);
   const int L = max(0, min(context_lens[s], a.max_context_len));
   const int P = (L + kPage - 1) / kPage;
-  const int p0 = j * a.cpp;
   const int p1 = min(p0 + a.cpp, P);
   if (p0 >= p1) return;  // empty split: nothing written, the merge skips it
   const int n_units = p1 - p0;
   const bool head_ok = n16 < a.G;
 
-  u4_t qraw[NG];
-  load_q<D>(a, s, h, n16, q4, qraw);
   // The wave that holds the sequence's last page writes the step's new token into it before it
   // requests that page (unit k_last of the wave).
-  const int32_t *btrow = block_tables + (int64_t)s * a.max_blocks;
   const int blk_last = btrow[P - 1];
-  const bool own_new = a.k_new != nullptr && p1 == P && wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
+  // (a length above max_context_len, outside the contract, writes nothing)
+  const bool own_new = a.k_new != nullptr && context_lens[s] <= a.max_context_len && p1 == P &&
+                       wave == (n_units - 1) % NW && blk_last >= 0 && blk_last < a.NB;
   const int k_last = (n_units - 1) / NW;
-  u2_t knew, vnew;
-  load_new_rows<D>(a, s, h, own_new, lane, knew, vnew);
   const int64_t page_new = (int64_t)blk_last * a.Hkv + h;
   const int t_new = (L - 1) & (kPage - 1);
   b8_t qop[NG];
@@ -1600,10 +1640,8 @@ void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_ta
   for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int voff = lane * 16;
-  auto page_index = [&](int p) -> int64_t {
-    const int b = min(max(btrow[p], 0), a.NB - 1);
-    return (int64_t)b * a.Hkv + h;
-  };
+  auto page_index_of = [&](int blk) -> int64_t { return (int64_t)min(max(blk, 0), a.NB - 1) * a.Hkv + h; };
+  auto page_index = [&](int p) -> int64_t { return page_index_of(btrow[min(p, a.max_blocks - 1)]); };
   u4_t kb[NG], vb[NG];
   auto load = [&](u4_t(&dst)[NG], const void *base, int64_t pg, bool ok) {
     const auto r = page_rsrc(base, pg, PAGE_B, ok ? PAGE_B : 0);
@@ -1611,10 +1649,15 @@ void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_ta
     for (int i = 0; i < NG; ++i) dst[i] = ld16_page<kStreamPolicy>(r, voff, 1024 * i);
   };
   int u = wave;
-  if (own_new && k_last == 0) write_new_bf16<D>(a, page_new, t_new, knew, vnew, lane);
+  // The owner's stores complete (vmcnt, in issue order) before it requests the page they go to:
+  // here when that page is its first, else before that page's K load below.
+  if (own_new && k_last == 0) {
+    write_new_bf16<D>(a, page_new, t_new, knew, vnew, lane);
+    wait_vmcnt<0>();
+  }
   {
     const bool ok = u < n_units;
-    const int64_t pg = page_index(ok ? p0 + u : p0);
+    const int64_t pg = page_index_of(blk0);
     load(kb, a.kc, pg, ok);
     load(vb, a.vc, pg, ok);
   }
@@ -1623,11 +1666,17 @@ void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_ta
     const int lim = min(L - (p0 + u) * kPage, kPage);
     const int un = u + NW;
     const bool next_ok = un < n_units;
-    const int64_t pgn = page_index(next_ok ? p0 + un : p0);
+    const int64_t pgn = page_index(p0 + un);
 
     f4_t score = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < NG; ++g) score = mfma_bf16(__builtin_bit_cast(b8_t, kb[g]), qop[g], score);
+    if (own_new && un == n_units - 1) {
+      // outstanding now: this page's V loads, issued after the stores unless this is the wave's
+      // first page (then the stores came after them)
+      if (k_last == 1) wait_vmcnt<0>();
+      else wait_vmcnt<NG>();
+    }
     load(kb, a.kc, pgn, next_ok);
 
     float x[4];
@@ -1716,38 +1765,65 @@ __device__ __forceinline__ float wave_sum(float x) {
   return (row_lane(x, 0) + row_lane(x, 16)) + (row_lane(x, 32) + row_lane(x, 48));
 }
 
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int NCH = D / 64;
+  // Every argument is read at the top in one batch: passed through an empty asm (tied operands, no
+  // side effects), they are all loaded before it.  Left alone, the compiler reads each one where it
+  // is first needed and waits there, which serialises round trips before the partials are requested.
+  float *o_part = a.o_part, *outp = a.out, *lsep = a.lse;
+  float2 *mlp = a.ml;
+  const int32_t *cl = a.context_lens;
+  int Hq = a.Hq, nq = a.nq, NS = a.NS, qchunk = a.qchunk, mcl = a.max_context_len, cpp = a.cpp;
+  asm("; merge arguments" : "+s"(o_part), "+s"(outp), "+s"(lsep), "+s"(mlp), "+s"(cl), "+s"(Hq), "+s"(nq), "+s"(NS),
+      "+s"(qchunk), "+s"(mcl), "+s"(cpp));
+  // (the compiler takes asm results as varying across lanes; they are not)
+  o_part = uniform_ptr(o_part);
+  outp = uniform_ptr(outp);
+  lsep = uniform_ptr(lsep);
+  mlp = uniform_ptr(mlp);
+  cl = uniform_ptr(cl);
+  Hq = __builtin_amdgcn_readfirstlane(Hq);
+  nq = __builtin_amdgcn_readfirstlane(nq);
+  NS = __builtin_amdgcn_readfirstlane(NS);
+  qchunk = __builtin_amdgcn_readfirstlane(qchunk);
+  mcl = __builtin_amdgcn_readfirstlane(mcl);
+  cpp = __builtin_amdgcn_readfirstlane(cpp);
   const int lane = threadIdx.x;
-  const int HQ = a.Hq * a.nq;  // output rows per sequence: (query token, query head)
+  const int HQ = Hq * nq;  // output rows per sequence: (query token, query head)
   const int chunk = blockIdx.x % NCH;
   const int hq = (blockIdx.x / NCH) % HQ;
   const int s = blockIdx.x / (NCH * HQ);
   const int c = chunk * 64 + lane;
   const int64_t orow = ((int64_t)s * HQ + hq);
-  const int64_t base = orow * a.NS;
+  const int64_t base = orow * NS;
   // buffer loads over this row's partials (past NS they return 0 and are masked below)
-  const auto rml = __builtin_amdgcn_make_buffer_rsrc(a.ml + base, 0, a.NS * 8, 0x00020000);
-  const auto ro = __builtin_amdgcn_make_buffer_rsrc(a.o_part + base * D, 0, a.NS * D * 4, 0x00020000);
+  const auto rml = __builtin_amdgcn_make_buffer_rsrc(mlp + base, 0, NS * 8, 0x00020000);
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc(o_part + base * D, 0, NS * D * 4, 0x00020000);
   // the row's query chunk attends over the keys up to its last query token: the context length
   // that sets the row's splits
-  const int Lc = a.context_lens[s];
-  const int qi = hq / a.Hq;  // query token of the row
-  const int c0 = qi - qi % a.qchunk, n_here = min(a.qchunk, a.nq - c0);
+  const int Lc = cl[s];
+  const int qi = hq / Hq;  // query token of the row
+  const int c0 = qi - qi % qchunk, n_here = min(qchunk, nq - c0);
   float M = -INFINITY, l = 0.0f, o = 0.0f;
-  for (int j0 = 0; j0 < a.NS; j0 += kMergeBlock) {
+  for (int j0 = 0; j0 < NS; j0 += kMergeBlock) {
     const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, lane * 8, j0 * 8, 0));
     float ov[kMergeBlock];
 #pragma unroll
     for (int u = 0; u < kMergeBlock; ++u)
       ov[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, c * 4, (j0 + u) * D * 4, 0));
-    // (kept in the loop, after the loads: hoisted out of it, the wait for the context length
-    // would come before the partials are requested)
-    int Lk = Lc;
-    asm volatile("" : "+s"(Lk));
-    const int L = max(0, min(max(0, min(Lk, a.max_context_len)) - a.nq + c0 + n_here, a.max_context_len));
-    const int nsa = min(a.NS, ((L + kPage - 1) / kPage + a.cpp - 1) / a.cpp);  // splits with pages
+    // (read here, after the partial loads are issued: the wait for the context length then does
+    // not hold them back)
+    const int Lk = __builtin_amdgcn_readfirstlane(Lc);
+    const int L = max(0, min(max(0, min(Lk, mcl)) - nq + c0 + n_here, mcl));
+    const int nsa = min(NS, ((L + kPage - 1) / kPage + cpp - 1) / cpp);  // splits with pages
     // splits past nsa were not written by this call: their (m, l, o) are masked, never multiplied
     const int nb = nsa - j0;
     const bool valid = lane < nb;
@@ -1769,11 +1845,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     M = Mn;
   }
   if (M == -INFINITY) {  // no split holds a key: empty context
-    a.out[orow * D + c] = 0.0f;
-    if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = -INFINITY;
+    outp[orow * D + c] = 0.0f;
+    if (lsep && chunk == 0 && lane == 0) lsep[orow] = -INFINITY;
   } else {
-    a.out[orow * D + c] = o / l;
-    if (a.lse && chunk == 0 && lane == 0) a.lse[orow] = kLn2 * (M + log2f(l));
+    outp[orow * D + c] = o / l;
+    if (lsep && chunk == 0 && lane == 0) lsep[orow] = kLn2 * (M + log2f(l));
   }
 }
 
@@ -1822,7 +1898,7 @@ static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
     hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, 0, FMT>), dim3(grid), dim3(NW * 64), smem, stream, a,
-                       a.block_tables);
+                       a.block_tables, a.context_lens);
   else
     hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
 }
@@ -1848,11 +1924,14 @@ static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   else if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
     hipLaunchKernelGGL((section_i8_kernel<D, 4, 2>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
   else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a, a.block_tables,
+                       a.context_lens);
   else if (a.rtw == 2)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables,
+                       a.context_lens);
   else
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 1, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 1, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables,
+                       a.context_lens);
 }
 
 // dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head
