@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["Cache", "KvqError", "write", "decode", "decode_mq", "choose_num_splits_mq", "decode_step", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
+__all__ = ["Cache", "KvqError", "write", "decode", "decode_mq", "choose_num_splits_mq", "decode_step", "decode_step_noalloc", "noalloc_max_bytes", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
            "status_string", "lib", "LIB_PATH", "INT8", "BF16", "INT8_HEAD"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -63,6 +63,10 @@ lib.kvq_decode_step.argtypes = _STEP
 lib.kvq_decode_step.restype = ctypes.c_int
 lib.kvq_check_decode_step.argtypes = _STEP
 lib.kvq_check_decode_step.restype = ctypes.c_int
+lib.kvq_decode_step_noalloc.argtypes = [_CP, _P, _P, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _P, _P, _P]
+lib.kvq_decode_step_noalloc.restype = ctypes.c_int
+lib.kvq_decode_step_noalloc_max_bytes.argtypes = []
+lib.kvq_decode_step_noalloc_max_bytes.restype = ctypes.c_size_t
 lib.kvq_decode_partials.argtypes = [_CP, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _P, ctypes.c_size_t, _P]
 lib.kvq_decode_partials.restype = ctypes.c_int
 lib.kvq_decode_merge.argtypes = [_CP, _P, _i32, _i32, _i32, _i32, _P, ctypes.c_size_t, _P, _P, _P]
@@ -216,6 +220,14 @@ def page_offset(dtype: int, head_dim: int, which: int, token: int, channel: int)
     return int(lib.kvq_page_offset(dtype, head_dim, which, token, channel))
 
 
+def _check_tables(what, block_tables, context_lens, S):
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError(f"{what}: block_tables and context_lens must be int32")
+    if not (block_tables.is_contiguous() and context_lens.is_contiguous()) or block_tables.dim() != 2 \
+            or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError(f"{what}: block_tables [S][max_blocks] and context_lens [S] required")
+
+
 def _decode_args(cache, q, block_tables, context_lens, max_context_len, num_splits, out, lse, workspace, want_lse):
     q = _as_bits16(q)
     S, Hq, D = (int(x) for x in q.shape)
@@ -309,6 +321,32 @@ def decode_step(cache: Cache, k_new, v_new, q, block_tables, context_lens, max_c
     fn = lib.kvq_check_decode_step if checked else lib.kvq_decode_step
     _check(fn(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), *args, _stream(stream)), "kvq_decode_step")
     return out, lse
+
+
+def decode_step_noalloc(cache: Cache, k_new, v_new, q, block_tables, context_lens, max_context_len: int,
+                        num_splits: int = 0, *, out, lse=None, stream=None) -> None:
+    """decode_step without a workspace: the library's fixed per-device buffer holds the partials
+    (kvq_decode_step_noalloc).  ``out`` (and ``lse`` if wanted) must be given: nothing is allocated."""
+    k_new, v_new, q = _as_bits16(k_new), _as_bits16(v_new), _as_bits16(q)
+    S, Hq, D = (int(x) for x in q.shape)
+    if D != cache.head_dim or not q.is_contiguous():
+        raise ValueError("q must be contiguous [S][Hq][D] bf16")
+    if tuple(k_new.shape) != (S, cache.num_kv_heads, D) or tuple(v_new.shape) != tuple(k_new.shape) \
+            or not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError(f"k_new/v_new must be contiguous [{S}][{cache.num_kv_heads}][{D}] bf16")
+    _check_tables("decode_step_noalloc", block_tables, context_lens, S)
+    if out is None:
+        raise ValueError("decode_step_noalloc: out must be given (nothing is allocated)")
+    _check_outputs("decode_step_noalloc", out, (S, Hq, D), lse, (S, Hq), None)
+    _on_device("decode_step_noalloc", k_new, v_new, q, block_tables, context_lens, out, lse, *_cache_planes(cache))
+    st = lib.kvq_decode_step_noalloc(ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(block_tables),
+                                     int(block_tables.shape[1]), _ptr(context_lens), int(max_context_len), S, Hq,
+                                     int(num_splits), _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "kvq_decode_step_noalloc")
+
+
+def noalloc_max_bytes() -> int:
+    return int(lib.kvq_decode_step_noalloc_max_bytes())
 
 
 def decode_partials(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int, workspace,

@@ -395,6 +395,31 @@ int kvq_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_n
                      num_seqs, num_q_heads, num_splits, out, lse, workspace, workspace_bytes_given, stream);
 }
 
+int kvq_decode_step_noalloc(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                            float *out, float *lse, void *stream) {
+  if (!k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+  // size check before the scratch is looked up: a call that needs more than the fixed buffer is
+  // refused with nothing enqueued
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = check_heads(cache, num_q_heads);
+  if (st != KVQ_OK) return st;
+  if (num_seqs <= 0 || max_context_len < 1 || num_splits < 0 || num_splits > kMaxSplits) return KVQ_ERR_INVALID_ARG;
+  const int ns = num_splits ? num_splits
+                            : choose_splits(cache->dtype, num_seqs, cache->num_kv_heads, cache->head_dim,
+                                            max_context_len, device_cus());
+  if (workspace_bytes(num_seqs, num_q_heads, ns, cache->head_dim) > kvq::kScratchBytes)
+    return KVQ_ERR_WORKSPACE_TOO_SMALL;
+  void *scratch = nullptr;
+  if (kvq::scratch_address(&scratch) != hipSuccess) return KVQ_ERR_LAUNCH_FAILED;
+  return decode_impl(cache, k_new, v_new, q, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                     num_seqs, num_q_heads, ns, out, lse, scratch, kvq::kScratchBytes, stream);
+}
+
+size_t kvq_decode_step_noalloc_max_bytes(void) { return kvq::kScratchBytes; }
+
 int kvq_check_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
                           const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
                           int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,

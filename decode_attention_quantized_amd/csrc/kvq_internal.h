@@ -37,6 +37,12 @@ struct DecodeArgs {
   int row_groups;                 // ceil(row_tiles / rtw): workgroups per (split, KV head, sequence)
 };
 
+// Bytes of the fixed device scratch used by kvq_decode_step_noalloc (the split partials).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+
+// Device address of the current device's fixed scratch (looked up once per device).
+hipError_t scratch_address(void **ptr);
+
 // Each returns hipSuccess or the launch error.  dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head.
 hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream);
 hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t stream);

@@ -20,6 +20,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "kvq_internal.h"
@@ -1851,6 +1852,36 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     outp[orow * D + c] = o / l;
     if (lsep && chunk == 0 && lane == 0) lsep[orow] = kLn2 * (M + log2f(l));
   }
+}
+
+// ------------------------------------------------------------------ fixed scratch
+//
+// Device scratch of kvq_decode_step_noalloc (for callers that cannot allocate): the split
+// partials live in this file-scope array instead of a caller's workspace.  Each device that loads
+// the library holds its own copy, zero-initialised when the code object is loaded, until the
+// process ends.  Host code must never pass the array's name to a kernel (on the host it names a
+// stand-in, not device memory): scratch_address() returns the device address of the current
+// device's copy, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void **ptr) {
+  constexpr int kMaxDevices = 64;
+  static void *addr[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------------ launchers

@@ -242,6 +242,26 @@ int kvq_decode_step(const kvq_cache_t *cache, const void *k_new, const void *v_n
                     float *out, float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kvq_decode_step for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace.  The split partials go to a fixed device buffer inside the library, one per device,
+ * of kvq_decode_step_noalloc_max_bytes() bytes (8 MiB), held from the first call on that device
+ * until the process ends.  A call whose partials would not fit (kvq_decode_workspace_bytes() with
+ * the split count used, num_splits or the automatic choice, above that size) returns
+ * KVQ_ERR_WORKSPACE_TOO_SMALL with nothing enqueued.  Allocates nothing (no hipMalloc, hipFree or
+ * allocating library call).  The buffer is shared by every call on the device: calls that overlap
+ * in time on one device (different streams, or host threads without ordering) race and give
+ * unspecified results.  Results equal kvq_decode_step's with the same split count.
+ */
+int kvq_decode_step_noalloc(const kvq_cache_t *cache, const void *k_new, const void *v_new, const void *q,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_splits,
+                            float *out, float *lse, void *stream);
+
+/* Size in bytes of the fixed device buffer kvq_decode_step_noalloc uses. */
+size_t kvq_decode_step_noalloc_max_bytes(void);
+
+/*
  * The two halves of kvq_decode_attention, for callers that combine partials themselves
  * (for instance partials of one sequence computed in several places) or time the split
  * kernel alone.  kvq_decode_partials writes, for every split that holds pages, the

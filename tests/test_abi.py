@@ -176,3 +176,16 @@ def test_split_heuristic_is_sane():
         assert ns <= max(1, pages)
     assert K.lib.kvq_choose_num_splits(ctypes.byref(_desc()), 1, 24, 0) == -1
     assert K.lib.kvq_choose_num_splits(ctypes.byref(_desc()), 1, 23, 64) == -1
+
+
+def test_noalloc_step_rejects_before_launch():
+    d = _desc()
+    f = K.lib.kvq_decode_step_noalloc
+    # missing new-token rows, bad head counts, bad split count: invalid before anything else
+    assert f(ctypes.byref(d), None, FAKE, FAKE, FAKE, 32, FAKE, 512, 1, 24, 4, FAKE, None, None) == -1
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 32, FAKE, 512, 1, 25, 4, FAKE, None, None) == -1
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 32, FAKE, 512, 1, 24, 5000, FAKE, None, None) == -1
+    # partials above the fixed buffer (64 x 32 heads x 64 splits x 258 floats): refused, nothing launched
+    d8 = _desc(hkv=8)
+    assert K.lib.kvq_decode_step_noalloc_max_bytes() == 8 << 20
+    assert f(ctypes.byref(d8), FAKE, FAKE, FAKE, FAKE, 32, FAKE, 512, 64, 32, 64, FAKE, None, None) == -3
