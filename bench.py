@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-multi-token", action="store_true", help="skip the several-query-token decode timings")
     p.add_argument("--no-int-qk", action="store_true", help="skip the integer Q.K timing")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the fused step of the 4K, mixed-batch and dense-8B workloads")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU seconds for the oracle sample")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     p.add_argument("--sweep", action="store_true",
@@ -212,9 +214,11 @@ def time_int_qk(torch, K, layers, S, Hq, mcl, ns, n_layers, steps, warmup):
     return res
 
 
-def time_multi_token(torch, K, layers, S, Hq, D, mcl, lens, Hkv, n_layers, steps, warmup):
+def time_multi_token(torch, K, layers, S, Hq, D, mcl, lens, Hkv, n_layers, steps, warmup, keep=None):
     """us per step (every layer: split + merge) of decode with n_q query tokens per sequence,
-    causal among them, at the library's split count; graph replay as for the main step."""
+    causal among them, at the library's split count; graph replay as for the main step.  keep (a
+    dict), if given, receives layer 1's queries and outputs of the 8-token decode and of the
+    prompt section, for the parity sample."""
     res = {}
     g = torch.Generator(device="cuda")
     g.manual_seed(1234)
@@ -229,6 +233,8 @@ def time_multi_token(torch, K, layers, S, Hq, D, mcl, lens, Hkv, n_layers, steps
             for L, (o, l) in zip(layers, outs):
                 K.decode_mq(L.cache, q, L.bt, L.lens, mcl, ns, out=o, lse=l, workspace=ws)
         ms, _ = time_step(torch, step, steps, warmup, False)
+        if keep is not None and nq == 8:
+            keep["mq8"] = (q.view(torch.int16).cpu().numpy().view(np.uint16), outs[0][0].cpu().numpy(), ns)
         res[str(nq)] = {"us_per_step": round(ms * 1e3, 1), "num_splits": ns,
                         "GB_per_s": round(algorithmic_bytes(lens, Hkv, D, "int8") * n_layers / (ms * 1e-3) / 1e9, 1)}
         log(f"int8 decode with {nq} query tokens: {ms * 1e3:.1f} us/step, splits {ns}")
@@ -244,23 +250,13 @@ def time_multi_token(torch, K, layers, S, Hq, D, mcl, lens, Hkv, n_layers, steps
     def section():
         K.decode_mq(layers[0].cache, q, layers[0].bt, layers[0].lens, mcl, ns, out=o, lse=lse, workspace=ws)
     ms, _ = time_step(torch, section, max(steps // 10, 3), 1, False)
+    if keep is not None:
+        keep["section"] = (q.view(torch.int16).cpu().numpy().view(np.uint16), o.cpu().numpy(), ns)
     flops = 4.0 * Hq * D * S * sum(L - nq + i + 1 for i in range(nq))
     res["prompt_section_2048"] = {"us_per_layer": round(ms * 1e3, 1), "num_splits": ns,
                                   "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1)}
     log(f"prompt section of {nq} tokens: {ms * 1e3:.1f} us per layer, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
     return res
-
-
-def sleep_cycles_for(torch, ms):
-    """torch.cuda._sleep spin length that takes about `ms` milliseconds on this GPU."""
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 1_000_000
-    e0.record()
-    torch.cuda._sleep(n)
-    e1.record()
-    torch.cuda.synchronize()
-    per = max(e0.elapsed_time(e1), 1e-3) / n
-    return int(ms / per)
 
 
 def time_split_kernel(torch, K, layers, mcl, ns, ws, passes):
@@ -432,14 +428,27 @@ def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
                      "4 KV heads, D 256)", FILL_TRAFFIC_SUMMARY)
 
 
+def oracle_cache_for(O, lay, k, v):
+    """The oracle's cache of one layer after the prefill and the step's token (what the GPU cache
+    holds after the fused step)."""
+    cfg = lay.cfg
+    oc = O.OracleCache.empty("int8", lay.num_blocks, cfg.num_kv_heads, cfg.head_dim)
+    pre, stp = lay.prefill_rows(), lay.step_rows()
+    O.kv_write(oc, k[pre], v[pre], lay.slots[pre])
+    O.kv_write(oc, k[stp], v[stp], lay.slots[stp])
+    return oc
+
+
 def cpu_baseline(host, states_int8, budget_s):
     """The oracle (as it stands) on the first layers of the workload until ~budget_s CPU seconds:
     kv_write of the step token plus decode of every query row of the layer.  Also returns the
-    largest deviation of the GPU's output for those layers from the oracle."""
+    largest deviation of the GPU's output for those layers from the oracle, and layer 1's oracle
+    cache (for the several-query-token parity sample)."""
     import oracle as O
 
     O.lib()
     elapsed, nbytes, layers_done, max_err, within = 0.0, 0, 0, 0.0, True
+    first = None
     for (lay, k, v, q), L in zip(host, states_int8):
         cfg = lay.cfg
         oc = O.OracleCache.empty("int8", lay.num_blocks, cfg.num_kv_heads, cfg.head_dim)
@@ -449,6 +458,8 @@ def cpu_baseline(host, states_int8, budget_s):
         O.kv_write(oc, k[stp], v[stp], lay.slots[stp])
         out, lse = O.decode(oc, q, lay.block_tables, lay.context_lens)
         elapsed += time.perf_counter() - t0
+        if first is None:
+            first = oc
         nbytes += algorithmic_bytes(lay.context_lens, cfg.num_kv_heads, cfg.head_dim, "int8")
         layers_done += 1
         g = L.out.cpu().numpy().astype(np.float64)
@@ -458,7 +469,38 @@ def cpu_baseline(host, states_int8, budget_s):
         log(f"oracle layer {layers_done}: {elapsed:.2f}s so far, gpu max abs err {err.max():.2e}")
         if elapsed >= budget_s:
             break
-    return elapsed, nbytes, layers_done, max_err, within
+    return elapsed, nbytes, layers_done, max_err, within, first
+
+
+def multi_token_parity(O, oc, lay, keep, n_section_tokens=16, seed=7):
+    """The several-query-token outputs the bench timed (layer 1, at the bench's launch
+    configuration) against the oracle: every row of the 8-token decode, and every head of a seeded
+    sample of the prompt section's query tokens (its first and last included).  Query token i of n
+    attends to the first L - n + i + 1 keys: the oracle's decode over that prefix."""
+    res = {}
+    L = int(lay.context_lens[0])
+    bt = lay.block_tables[:1]
+    for name, sel in (("decode_8_tokens", None), ("prompt_section_2048", n_section_tokens)):
+        key = "mq8" if name == "decode_8_tokens" else "section"
+        if key not in keep:
+            continue
+        q, out, ns = keep[key]                  # q [1][n][Hq][D] bits, out [1][n][Hq][D]
+        n = q.shape[1]
+        if sel is None:
+            toks = np.arange(n)
+        else:
+            rng = np.random.default_rng(seed)
+            toks = np.unique(np.concatenate([[0, n - 1], rng.choice(n, sel - 2, replace=False)]))
+        lens = (L - n + 1 + toks).astype(np.int32)
+        ref, ref_lse = O.decode(oc, np.ascontiguousarray(q[0, toks]), np.repeat(bt, len(toks), axis=0), lens)
+        g = out[0, toks].astype(np.float64)
+        err = np.abs(g - ref)
+        ok = bool(np.all(err <= 2e-3 + 1e-3 * np.abs(ref)))
+        res[name] = {"query_tokens_checked": int(len(toks)), "rows": int(len(toks) * q.shape[2]),
+                     "num_splits": int(ns), "max_abs_err": float(err.max()), "within_tolerance": ok}
+        log(f"parity sample {name}: {len(toks)} query tokens, max abs err {err.max():.3e}"
+            + ("" if ok else " OUT OF TOLERANCE"))
+    return res
 
 
 def cpu_baseline_one_thread(host):
@@ -484,6 +526,90 @@ def cpu_baseline_one_thread(host):
 
 
 FLUSH_BYTES = 512 << 20  # written between steps when the whole cache fits in the 256 MB MALL
+
+
+def time_graph_median(torch, step, steps, warmup, flush=None):
+    """Median us of one graph replay of `step` over `steps` replays (HIP events on the replay
+    stream around each replay); with `flush`, a fill of that buffer before every replay (outside
+    the timed region) evicts the caches from the MALL."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+        times = []
+        for i in range(warmup + steps):
+            if flush is not None:
+                flush.fill_(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            graph.replay()
+            e1.record(s)
+            if i >= warmup:
+                times.append((e0, e1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in times])) * 1e3
+
+
+def other_workloads(torch, K, W, cids, steps, warmup, parity):
+    """The fused step (every layer: decode_split with the new token's write, then decode_merge) of
+    the other workloads at the library's split count, each prepared, timed and freed in turn: us
+    per step, algorithmic GB/s and % of 8 TB/s.  Workloads whose caches would fit in the 256 MB
+    MALL get a 512 MiB fill between replays.  With `parity`, layer 1's output is compared with the
+    oracle."""
+    res = {}
+    for cid in cids:
+        cfg = W.CONFIGS[cid]
+        states, host, lay, _ = prepare(cid, cfg.layers, ["int8"], 1 if parity else 0)
+        layers = states["int8"]
+        S, Hq, Hkv, D = lay.S, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+        mcl = int(lay.context_lens.max())
+        ns = K.choose_num_splits(layers[0].cache, S, Hq, mcl)
+        ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
+        step_bytes = sum(algorithmic_bytes(L_.lens.cpu().numpy(), Hkv, D, "int8") for L_ in layers)
+        flush = None
+        if algorithmic_bytes(lay.context_lens, Hkv, D, "bf16") * cfg.layers < 2 * FLUSH_BYTES:
+            flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        us = time_graph_median(torch, make_step(K, layers, S, Hq, mcl, ns, ws), steps, warmup, flush)
+        gbs = step_bytes / (us * 1e-6) / 1e9
+        r = {"us_per_step": round(us, 1), "GB_per_s": round(gbs, 1), "pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 1),
+             "num_splits": ns, "layers": cfg.layers, "batch": S,
+             "context": f"{int(lay.context_lens.min())}..{mcl}" if S > 1 else mcl,
+             "heads": f"{Hq}/{Hkv}", "head_dim": D, "algorithmic_bytes_per_step": int(step_bytes),
+             "mall_flushed": flush is not None}
+        log(f"{cfg.name}: {us:.1f} us/step, {gbs:.0f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of peak), splits {ns}")
+        if parity:
+            import oracle as O
+            lay0, k, v, q = host[0]
+            oc = oracle_cache_for(O, lay0, k, v)
+            ref, _ = O.decode(oc, q, lay0.block_tables, lay0.context_lens)
+            g = layers[0].out.cpu().numpy().astype(np.float64)
+            err = np.abs(g - ref)
+            r["parity_layer1"] = {"max_abs_err": float(err.max()),
+                                  "within_tolerance": bool(np.all(err <= 2e-3 + 1e-3 * np.abs(ref)))}
+            log(f"{cfg.name} layer 1 against the oracle: max abs err {err.max():.3e}")
+        res[cfg.name] = r
+        del states, host, layers, ws, flush
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_info():
+    """The host CPU's model name (from /proc/cpuinfo) and os.cpu_count()."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
 
 
 def sweep(args):
@@ -596,10 +722,13 @@ def main():
                                   args.warmup, args.eager)
         ms, wall_ms = time_step(torch, make_step(K, layers, S, Hq, mcl, ns, ws), args.steps, args.warmup,
                                 args.eager)
+        # noise control: the same step captured and timed again (auto split count both times)
+        ms_rep, _ = time_step(torch, make_step(K, layers, S, Hq, mcl, ns, ws), args.steps, args.warmup,
+                              args.eager)
         step_bytes = algorithmic_bytes(lens, Hkv, D, d) * n_layers
         kern_us = time_split_kernel(torch, K, layers, mcl, ns, ws, passes=max(args.steps, 20))
         results[d] = dict(ms=ms, wall_ms=wall_ms, ms_unfused=ms_unfused, ns=ns, step_bytes=step_bytes,
-                          kern_us=kern_us, layer_bytes=algorithmic_bytes(lens, Hkv, D, d))
+                          kern_us=kern_us, layer_bytes=algorithmic_bytes(lens, Hkv, D, d), ms_rep=ms_rep)
         log(f"{d}: {ms * 1e3:.1f} us/step (wall {wall_ms * 1e3:.1f}; three kernels per layer "
             f"{ms_unfused * 1e3:.1f}), {step_bytes / ms / 1e6:.0f} GB/s, decode_split {kern_us:.2f} us/launch, "
             f"splits {ns}")
@@ -618,6 +747,9 @@ def main():
         "us_per_step": round(r["ms"] * 1e3, 1),
         "us_per_step_unfused": round(r["ms_unfused"] * 1e3, 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 1),
+        "noise_control": {"what": "the same fused step (auto split count) captured and timed a second time",
+                          "us_per_step_repeat": round(r["ms_rep"] * 1e3, 1),
+                          "spread_pct": round(100 * abs(r["ms_rep"] - r["ms"]) / r["ms"], 2)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -673,12 +805,14 @@ def main():
     if not args.no_int_qk:
         out["int8_qk_variant"] = time_int_qk(torch, K, states["int8"], S, Hq, mcl, r["ns"], n_layers,
                                              args.steps, args.warmup)
+    keep = {}
     if not args.no_multi_token:
         out["multi_token"] = time_multi_token(torch, K, states["int8"], S, Hq, D, mcl, lens, Hkv, n_layers,
-                                              args.steps, args.warmup)
+                                              args.steps, args.warmup, keep)
     if not args.no_cpu_baseline:
-        el, nb, nl, max_err, within = cpu_baseline(host, states["int8"], args.cpu_budget_s)
+        el, nb, nl, max_err, within, oc1 = cpu_baseline(host, states["int8"], args.cpu_budget_s)
         import oracle as O
+        model, ncpu = cpu_info()
         out["cpu_baseline"] = {
             "value": round(nb / el / 1e9, 4),
             "unit": "GB/s",
@@ -686,6 +820,8 @@ def main():
             "kind": "oracle",
             "sample": f"{nl} of {n_layers} layers: kv_write of the step token + fp64 decode of all {S * Hq} "
                       f"query rows per layer ({el:.1f} s)",
+            "cpu_model": model,
+            "os_cpu_count": ncpu,
         }
         el1, nb1 = cpu_baseline_one_thread(host)
         out["cpu_baseline"]["one_thread"] = {"value": round(nb1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
@@ -693,6 +829,15 @@ def main():
         out["parity_sample"] = {"layers": nl, "max_abs_err": max_err, "within_tolerance": within}
         log(f"parity sample ({nl} layers, fused step against the oracle): max abs err {max_err:.3e}, "
             + ("within tolerance" if within else "OUT OF TOLERANCE"))
+        if keep:
+            out["parity_sample"]["several_query_tokens"] = multi_token_parity(O, oc1, host[0][0], keep)
+    if not args.no_other_workloads and args.config == 3 and not args.layers:
+        # free the 32K workload first: the others are prepared one at a time
+        del states, host
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["other_workloads"] = other_workloads(torch, K, W, [2, 4, 5], max(args.steps // 2, 20), args.warmup,
+                                                 not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
 

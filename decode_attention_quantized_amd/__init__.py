@@ -233,11 +233,7 @@ def _decode_args(cache, q, block_tables, context_lens, max_context_len, num_spli
     S, Hq, D = (int(x) for x in q.shape)
     if D != cache.head_dim or not q.is_contiguous():
         raise ValueError("q must be contiguous [S][Hq][D] bf16")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
-    if not (block_tables.is_contiguous() and context_lens.is_contiguous()) or block_tables.dim() != 2 \
-            or block_tables.shape[0] != S or context_lens.shape != (S,):
-        raise ValueError("block_tables [S][max_blocks] and context_lens [S] required")
+    _check_tables("decode", block_tables, context_lens, S)
     _check_outputs("decode", out, (S, Hq, D), lse, (S, Hq), workspace)
     _on_device("decode", q, block_tables, context_lens, out, lse, workspace, *_cache_planes(cache))
     ns = num_splits if num_splits else choose_num_splits(cache, S, Hq, max_context_len)
@@ -352,7 +348,11 @@ def noalloc_max_bytes() -> int:
 def decode_partials(cache: Cache, q, block_tables, context_lens, max_context_len: int, num_splits: int, workspace,
                     *, stream=None) -> None:
     """First half of decode: split partials into ``workspace`` (num_splits must be explicit)."""
+    q = _as_bits16(q)
+    if q.dim() != 3 or int(q.shape[2]) != cache.head_dim or not q.is_contiguous():
+        raise ValueError("decode_partials: q must be contiguous [S][Hq][D] bf16 with D the cache's head_dim")
     S, Hq, _ = (int(x) for x in q.shape)
+    _check_tables("decode_partials", block_tables, context_lens, S)
     _check_outputs("decode_partials", None, (), None, (), workspace)
     _on_device("decode_partials", q, block_tables, context_lens, workspace, *_cache_planes(cache))
     st = lib.kvq_decode_partials(ctypes.byref(cache.desc), _ptr(q), _ptr(block_tables), int(block_tables.shape[1]),
@@ -364,6 +364,11 @@ def decode_partials(cache: Cache, q, block_tables, context_lens, max_context_len
 def decode_merge(cache: Cache, context_lens, max_context_len: int, num_seqs: int, num_q_heads: int, num_splits: int,
                  workspace, out, lse=None, *, stream=None) -> None:
     """Second half of decode: combine the partials in ``workspace`` into out (and lse)."""
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous() \
+            or tuple(context_lens.shape) != (int(num_seqs),):
+        raise ValueError("decode_merge: context_lens must be contiguous int32 [num_seqs]")
+    if out is None:
+        raise ValueError("decode_merge: out must be given")
     _check_outputs("decode_merge", out, (num_seqs, num_q_heads, cache.head_dim), lse, (num_seqs, num_q_heads),
                    workspace)
     _on_device("decode_merge", context_lens, workspace, out, lse)

@@ -135,17 +135,23 @@ int kvq_write(const kvq_cache_t *cache, const void *k, const void *v, const int3
 /*
  * Bytes of workspace kvq_decode_attention needs for these sizes; num_splits is the split
  * count actually used (1..4096; for the automatic choice pass kvq_choose_num_splits()'s
- * result).  The workspace holds the split partials: fp32 weighted sums [S][Hq][splits][D]
- * (256-byte aligned) followed by (max, sum) pairs [S][Hq][splits][2].  Returns 0 on invalid
- * arguments.
+ * result).  The workspace holds what each segment of the context hands to the combination step
+ * (long-context page, section "Give more GPU workers a piece of the attention calculation": a
+ * weighted value sum and its normalisation terms per segment): fp32 weighted sums
+ * [S][Hq][splits][D] (256-byte aligned) followed by (max, sum) pairs [S][Hq][splits][2].
+ * Returns 0 on invalid arguments.
  */
 size_t kvq_decode_workspace_bytes(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_splits);
 
 /*
- * Split count the library uses when kvq_decode_attention gets num_splits == 0.  Depends only
- * on the host-side sizes and the device's compute-unit count (no device synchronisation).
- * Returns a negative kvq_status_t on invalid arguments.
+ * Split count the library uses when kvq_decode_attention gets num_splits == 0.  Long-context
+ * page, section "Split count": the best number of segments depends on the context length and is
+ * found by sweeping it; section "Give more GPU workers a piece of the attention calculation":
+ * segments exist to give every compute unit work.  Here: enough workgroups to fill the device's
+ * compute units, no segment shorter than 8 pages, from sweeps on 256 CUs.  Depends only on the
+ * host-side sizes and the device's compute-unit count (no device synchronisation).  Returns a
+ * negative kvq_status_t on invalid arguments.
  */
 int32_t kvq_choose_num_splits(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
                               int32_t max_context_len);
@@ -156,7 +162,8 @@ int32_t kvq_choose_num_splits(const kvq_cache_t *cache, int32_t num_seqs, int32_
  *   block_tables       device, int32 [num_seqs][max_blocks_per_seq].
  *   context_lens       device, int32 [num_seqs]; tokens 0..context_lens[s]-1 are attended
  *                      (the token written by this step's kvq_write included); must satisfy
- *                      0 <= context_lens[s] <= max_context_len.
+ *                      0 <= context_lens[s] <= max_context_len.  A length of 0 (a slot of the
+ *                      batch with no tokens yet) is accepted and gives out = 0, lse = -inf.
  *   max_context_len    host: upper bound of context_lens, sizes the grid without a sync;
  *                      1 <= max_context_len <= max_blocks_per_seq*16.
  *   num_splits         0 = automatic (kvq_choose_num_splits), else 1..4096.
@@ -231,7 +238,9 @@ int32_t kvq_choose_num_splits_mq(const kvq_cache_t *cache, int32_t num_seqs, int
  *                  at position context_lens[s]-1 of each sequence.
  *   other arguments as kvq_decode_attention (same workspace size).
  * A sequence with context_lens[s] == 0 writes nothing; nothing is written when the block of the
- * last page is outside [0, num_blocks).  Contract (checked by kvq_check_decode_step): the block
+ * last page is outside [0, num_blocks), nor when context_lens[s] > max_context_len (outside the
+ * contract: the context is then cut at max_context_len for memory safety, and the token, whose
+ * position lies past the cut, is not written anywhere).  Contract (checked by kvq_check_decode_step): the block
  * that receives a sequence's new token is not used by any other sequence of the call, and not
  * twice in that sequence's table (blocks shared between sequences hold only older tokens).
  * Asynchronous on `stream`; allocates nothing.

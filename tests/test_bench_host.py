@@ -117,3 +117,30 @@ def test_fill_traffic_summary(tmp_path, monkeypatch):
     assert rec["algorithmic_bytes_per_launch"] == bench.fill_bytes(32767, 4, 256, "int8")
     # the decode_split record is unaffected by the writer's dispatches
     assert bench.measured_traffic()["fetch_bytes_per_launch"] == int(35000.0 * 1024 * 2)
+
+
+def test_cpu_info_names_the_host():
+    model, n = bench.cpu_info()
+    assert n == os.cpu_count()
+    assert model is None or isinstance(model, str)
+
+
+def test_multi_token_parity_sample_uses_each_query_tokens_prefix():
+    # the sample compares query token i of n with the oracle's decode over the first L - n + i + 1
+    # keys: fed the oracle's own causal result it passes, and a row computed over one key too many
+    # (the whole context for every token) fails
+    import oracle as O
+    lay = W.make_layer(1, 0)
+    cfg = lay.cfg
+    oc = bench.oracle_cache_for(O, lay, lay.k, lay.v)
+    n = 8
+    rng = np.random.default_rng(3)
+    q = W.f32_to_bf16_bits(rng.standard_normal((1, n, cfg.num_q_heads, cfg.head_dim)).astype(np.float32))
+    good, _ = O.decode_mq(oc, q, lay.block_tables, lay.context_lens)
+    res = bench.multi_token_parity(O, oc, lay, {"mq8": (q, good.astype(np.float32), 4)})
+    assert res["decode_8_tokens"]["within_tolerance"] and res["decode_8_tokens"]["rows"] == n * cfg.num_q_heads
+    full, _ = O.decode(oc, q.reshape(n, cfg.num_q_heads, cfg.head_dim), np.repeat(lay.block_tables, n, axis=0),
+                       np.repeat(lay.context_lens, n))
+    bad = full.reshape(good.shape).astype(np.float32)
+    res = bench.multi_token_parity(O, oc, lay, {"mq8": (q, bad, 4)})
+    assert not res["decode_8_tokens"]["within_tolerance"]

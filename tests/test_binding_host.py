@@ -43,3 +43,37 @@ def test_output_buffers_are_checked():
         K.decode_mq(cache, q[:, None], bt, cl, 10, 1, out=torch.zeros((1, 2, 128)))
     with pytest.raises(ValueError, match="workspace"):
         K.decode(cache, q, bt, cl, 10, 1, workspace=torch.zeros((64, 64), dtype=torch.uint8).t())
+
+
+def test_partials_and_merge_check_their_inputs():
+    # the library sizes its Q reads from the cache's head_dim and reads int32 tables: a smaller D,
+    # 64-bit tables or lengths, or a strided tensor must be refused before the library is called
+    cache, q, bt, cl = _host_problem()
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="head_dim"):
+        K.decode_partials(cache, torch.zeros((1, 2, 64), dtype=torch.bfloat16), bt, cl, 10, 1, ws)
+    with pytest.raises(ValueError, match="head_dim"):
+        K.decode_partials(cache, torch.zeros((1, 128, 2), dtype=torch.bfloat16).transpose(1, 2), bt, cl, 10, 1, ws)
+    with pytest.raises(ValueError, match="int32"):
+        K.decode_partials(cache, q, bt.to(torch.int64), cl, 10, 1, ws)
+    with pytest.raises(ValueError, match="int32"):
+        K.decode_partials(cache, q, bt, cl.to(torch.int64), 10, 1, ws)
+    with pytest.raises(ValueError, match="required"):
+        K.decode_partials(cache, q, torch.zeros((1, 8), dtype=torch.int32)[:, ::2], cl, 10, 1, ws)
+    with pytest.raises(ValueError, match="context_lens"):
+        K.decode_merge(cache, cl.to(torch.int64), 10, 1, 2, 1, ws, torch.zeros((1, 2, 128)))
+    with pytest.raises(ValueError, match="context_lens"):
+        K.decode_merge(cache, torch.zeros(2, dtype=torch.int32), 10, 1, 2, 1, ws, torch.zeros((1, 2, 128)))
+    with pytest.raises(ValueError, match="out must be"):
+        K.decode_merge(cache, cl, 10, 1, 2, 1, ws, torch.zeros((1, 2, 64)))
+
+
+def test_noalloc_step_checks_its_inputs():
+    cache, q, bt, cl = _host_problem()
+    kv = torch.zeros((1, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out must be given"):
+        K.decode_step_noalloc(cache, kv, kv, q, bt, cl, 10, 1, out=None)
+    with pytest.raises(ValueError, match="int32"):
+        K.decode_step_noalloc(cache, kv, kv, q, bt.to(torch.int64), cl, 10, 1, out=torch.zeros((1, 2, 128)))
+    with pytest.raises(ValueError, match="GPU"):
+        K.decode_step_noalloc(cache, kv, kv, q, bt, cl, 10, 1, out=torch.zeros((1, 2, 128)))

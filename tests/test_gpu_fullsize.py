@@ -55,3 +55,44 @@ def test_fullsize_bf16_long_context():
                             int(layer.context_lens.max()), ns)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref[0], ref[1], f"config 3 bf16 ns={ns}")
+
+
+def _mq_queries(n, Hq, D, seed):
+    """Seeded bf16 queries [1][n][Hq][D] with the workloads' x20 outlier channels."""
+    rng = np.random.default_rng(seed)
+    mult = np.ones((Hq, D), np.float32)
+    for h in range(Hq):
+        mult[h, rng.choice(D, 4, replace=False)] = 20
+    return W.f32_to_bf16_bits((rng.standard_normal((1, n, Hq, D)) * mult).astype(np.float32))
+
+
+@pytest.mark.parametrize("nq,sample", [(8, None), (2048, 24)])
+def test_fullsize_several_query_tokens(nq, sample):
+    """The long-context layer with n_q query tokens at the end of the sequence, in the launch
+    configuration the benchmark times (automatic split count): 8 tokens (a verification step) and a
+    2048-token prompt section.  Every row of the 8-token decode, and every head of a seeded sample
+    of the section's query tokens (first and last included), against the oracle: query token i of n
+    attends to the first L - n + i + 1 keys."""
+    layer = W.make_layer(3, 0)
+    cfg = layer.cfg
+    Hq, D = cfg.num_q_heads, cfg.head_dim
+    pair = Pair("int8", layer.num_blocks, cfg.num_kv_heads, D)
+    log(f"n_q {nq}: writing")
+    fill_from_layer(pair, layer)
+    L = int(layer.context_lens[0])
+    q = _mq_queries(nq, Hq, D, 100 + nq)
+    ns = K.choose_num_splits_mq(pair.g, 1, nq, Hq, L)
+    log(f"n_q {nq}: decode_mq at {ns} splits")
+    out, lse = K.decode_mq(pair.g, bf16_dev(q), dev(layer.block_tables), dev(layer.context_lens), L, 0)
+    torch.cuda.synchronize()
+    if sample is None:
+        toks = np.arange(nq)
+    else:
+        rng = np.random.default_rng(nq)
+        toks = np.unique(np.concatenate([[0, nq - 1], rng.choice(nq, sample - 2, replace=False)]))
+    lens = (L - nq + 1 + toks).astype(np.int32)
+    log(f"n_q {nq}: oracle over {len(toks)} query tokens")
+    ref, ref_lse = O.decode(pair.o, np.ascontiguousarray(q[0, toks]), np.repeat(layer.block_tables, len(toks), axis=0),
+                            lens)
+    assert_close(out.cpu().numpy()[0, toks], lse.cpu().numpy()[0, toks], ref, ref_lse,
+                 f"long-context layer, {nq} query tokens, {ns} splits")

@@ -169,3 +169,24 @@ def test_checked_step_rejects_contract_violations():
     assert ei.value.status == -5
     with pytest.raises(ValueError):
         K.decode_step(pair.g, kd[:1], vd, qd, dev(bt), ld, 40, 2)
+
+
+@pytest.mark.parametrize("dtype", ["int8", "int8_head", "bf16"])
+def test_step_length_above_max_context_writes_nothing(dtype):
+    """A context length above max_context_len breaks the contract; the step must still not write
+    that sequence's token anywhere (its output is unspecified).  The other sequences' tokens are
+    written as usual: the cache equals a copy given only those tokens through kvq_write."""
+    pair, q, bt, lens, kn, vn = _problem(1500, [100, 200, 37], 24, 4, 256, dtype, spare=4)
+    g = pair.g
+    ref = K.Cache(dtype, g.num_blocks, 4, 256)
+    planes = lambda c: [t for t in (c.k, c.v, c.k_scales, c.v_scales) if t is not None]
+    for a, b in zip(planes(ref), planes(g)):
+        a.copy_(b)
+    slots = _new_slots(bt, lens)
+    slots[1] = -1  # sequence 1 (200 tokens) is above max_context_len 150: not written
+    K.write(ref, bf16_dev(kn), bf16_dev(vn), dev(slots))
+    K.decode_step(g, bf16_dev(kn), bf16_dev(vn), bf16_dev(q), dev(bt), dev(lens), 150, 4)
+    torch.cuda.synchronize()
+    for a, b in zip(planes(ref), planes(g)):
+        assert torch.equal(a.view(torch.int8) if a.element_size() == 1 else a.view(torch.int16 if a.element_size() == 2 else torch.int32),
+                           b.view(torch.int8) if b.element_size() == 1 else b.view(torch.int16 if b.element_size() == 2 else torch.int32))
