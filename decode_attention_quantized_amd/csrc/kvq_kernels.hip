@@ -783,9 +783,13 @@ __device__ __forceinline__ void write_partial(const DecodeArgs &a, int s, int h,
     // chunk's n_here * G real rows map past the end of the resources and their stores are dropped.
     const int64_t seq0 = (int64_t)s * a.nq * a.Hq * a.NS;  // first partial row of the sequence
     const int rows_valid = a.nq * a.Hq * a.NS;
+    // (an opaque copy of G: the division's constants are recomputed here, not kept live from the
+    // caller's prologue)
+    int Gd = G;
+    asm volatile("" : "+s"(Gd));
     auto row_offset = [&](int r) -> int {
       const int row = 16 * rt + r;
-      const int t = row / G, g = row - t * G;
+      const int t = row / Gd, g = row - t * Gd;
       return row < n_here * G ? ((c0 + t) * a.Hq + h * G + g) * a.NS + j : rows_valid;
     };
     if (q4 == 0) {  // (m, l) of row n16 (the same in the row's 4 lanes)
@@ -1583,7 +1587,14 @@ void section_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
       issue((b + 1) % NBUF, k + 1 + NBUF);
     }
   }
-  write_partial<D, NW, true, NW>(a, s, h, j, wave, n16, q4, m_run, l_run, acc, nullptr, rt, c0, n_here);
+  // The epilogue takes its lane indices from a fresh lane count (behind an opaque mask, so that it
+  // is not merged with the prologue's): keeping the prologue's lane-derived values live across the
+  // page loop would push them out of the capped register budget.
+  unsigned all = ~0u;
+  asm volatile("" : "+s"(all));
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u));
+  write_partial<D, NW, true, NW>(a, s, h, j, wave, lane_e & 15, lane_e >> 4, m_run, l_run, acc, nullptr, rt, c0,
+                                 n_here);
 }
 
 // ---- BF16 cache: 1-page units, bf16 MFMA (Q.K exact; P as bf16 hi + lo)
