@@ -61,6 +61,9 @@ def parse():
     p.add_argument("--sweep", action="store_true",
                    help="time the step at each of the workload's split counts and the automatic one")
     p.add_argument("--sweep-out", default="", help="also write the sweep table (markdown) to this path")
+    p.add_argument("--context-lens", default="",
+                   help="with --sweep: comma-separated context lengths replacing the workload's (same heads, "
+                        "head dim and layers), e.g. 32768,32768,32768,32768 for a uniform batch")
     p.add_argument("--pmc-workload", action="store_true",
                    help="run only the calibration copy and the decode_split launches (under rocprofv3 --pmc)")
     p.add_argument("--pmc-summarize", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CMD_FETCH", "CMD_WRITE"),
@@ -329,7 +332,7 @@ def pmc_workload(args):
     S, Hq = lay.S, cfg.num_q_heads
     mcl = int(lay.context_lens.max())
     layers = states["int8"]
-    ns = args.splits or K.choose_num_splits(layers[0].cache, S, Hq, mcl)
+    ns = args.splits or K.choose_num_splits_lengths(layers[0].cache, lay.context_lens, Hq)
     ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
     src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
@@ -567,7 +570,7 @@ def other_workloads(torch, K, W, cids, steps, warmup, parity):
         layers = states["int8"]
         S, Hq, Hkv, D = lay.S, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
         mcl = int(lay.context_lens.max())
-        ns = K.choose_num_splits(layers[0].cache, S, Hq, mcl)
+        ns = K.choose_num_splits_lengths(layers[0].cache, lay.context_lens, Hq)
         ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
         step_bytes = sum(algorithmic_bytes(L_.lens.cpu().numpy(), Hkv, D, "int8") for L_ in layers)
         flush = None
@@ -621,6 +624,13 @@ def sweep(args):
     import workloads as W
 
     torch.cuda.set_device(0)
+    if args.context_lens:
+        import dataclasses
+        lens = tuple(int(x) for x in args.context_lens.split(","))
+        base = W.CONFIGS[args.config]
+        name = f"{base.name} with lengths {args.context_lens}"
+        W.CONFIGS[args.config] = base._replace(name=name, context_lens=lens, seeded_lens=None) \
+            if hasattr(base, "_replace") else dataclasses.replace(base, name=name, context_lens=lens, seeded_lens=None)
     cfg = W.CONFIGS[args.config]
     n_layers = args.layers or cfg.layers
     dtypes = ["int8"] if args.no_bf16 else ["int8", "bf16"]
@@ -633,8 +643,10 @@ def sweep(args):
     rows = []
     for d in dtypes:
         layers = states[d]
-        auto = K.choose_num_splits(layers[0].cache, S, Hq, mcl)
-        counts = sorted(set(list(cfg.splits) + [auto]))
+        # the library's choice from the batch's lengths, and from the maximum length alone
+        auto = K.choose_num_splits_lengths(layers[0].cache, lay.context_lens, Hq)
+        auto_max = K.choose_num_splits(layers[0].cache, S, Hq, mcl)
+        counts = sorted(set(list(cfg.splits) + [auto, auto_max]))
         step_bytes = algorithmic_bytes(lay.context_lens, Hkv, D, d) * n_layers
         for ns in counts:
             ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
@@ -659,23 +671,27 @@ def sweep(args):
                         times.append((e0, e1))
             torch.cuda.synchronize()
             us = float(np.median([a.elapsed_time(b) for a, b in times])) * 1e3
-            rows.append((d, ns, ns == auto, us, step_bytes / (us * 1e-6) / 1e9))
-            log(f"{d} splits {ns}{' (auto)' if ns == auto else ''}: {us:.1f} us/step, {rows[-1][4]:.0f} GB/s")
+            mark = "/".join(m for m, x in (("lengths", auto), ("max only", auto_max)) if ns == x)
+            rows.append((d, ns, mark, us, step_bytes / (us * 1e-6) / 1e9))
+            log(f"{d} splits {ns}{f' (auto: {mark})' if mark else ''}: {us:.1f} us/step, {rows[-1][4]:.0f} GB/s")
             del graph, ws
     text = [f"# Split-count sweep: {cfg.name} ({n_layers} layers, batch {S}, context "
             f"{'/'.join(str(int(x)) for x in np.unique(lay.context_lens)) if S <= 8 else f'{int(lay.context_lens.min())}..{mcl}'}, "
             f"{Hq}/{Hkv} heads, D {D})", "",
             "Command (run from the repository root on one MI355X):", "", "```",
             f"python3 bench.py --sweep --config {args.config} --steps {args.steps} --warmup {args.warmup}"
+            + (f" --context-lens {args.context_lens}" if args.context_lens else "")
             + (" --no-bf16" if args.no_bf16 else "") + (f" --sweep-out {args.sweep_out}" if args.sweep_out else ""),
             "```", "",
             "Median over the timed steps of one graph replay of the fused step (every layer: decode_split with "
             "the new token's write, then decode_merge), HIP events on the replay stream."
             + (f"  A {FLUSH_BYTES >> 20} MiB fill between replays evicts the caches from the 256 MB MALL "
                "(outside the timed region)." if flush is not None else ""), "",
+            "", "auto: the library's choice from the batch's lengths (kvq_choose_num_splits_lengths, what the "
+            "benchmark uses) and from the maximum length alone (kvq_choose_num_splits, num_splits = 0).", "",
             "| cache | splits | auto | us per step | GB/s (algorithmic) |", "|---|---|---|---|---|"]
     for d, ns, a, us, gbs in rows:
-        text.append(f"| {d} | {ns} | {'yes' if a else ''} | {us:.1f} | {gbs:.0f} |")
+        text.append(f"| {d} | {ns} | {a} | {us:.1f} | {gbs:.0f} |")
     if args.sweep_out:
         with open(args.sweep_out, "w") as f:
             f.write("\n".join(text) + "\n")
@@ -716,7 +732,7 @@ def main():
     results = {}
     for d in dtypes:
         layers = states[d]
-        ns = args.splits or K.choose_num_splits(layers[0].cache, S, Hq, mcl)
+        ns = args.splits or K.choose_num_splits_lengths(layers[0].cache, lay.context_lens, Hq)
         ws = torch.empty(K.workspace_bytes(layers[0].cache, S, Hq, ns), dtype=torch.uint8, device="cuda")
         ms_unfused, _ = time_step(torch, make_step(K, layers, S, Hq, mcl, ns, ws, fused=False), args.steps,
                                   args.warmup, args.eager)

@@ -16,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["Cache", "KvqError", "write", "decode", "decode_mq", "choose_num_splits_mq", "decode_step", "decode_step_noalloc", "noalloc_max_bytes", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "page_offset",
+__all__ = ["Cache", "KvqError", "write", "decode", "decode_mq", "choose_num_splits_mq", "decode_step", "decode_step_noalloc", "noalloc_max_bytes", "decode_partials", "decode_merge", "workspace_bytes", "choose_num_splits", "choose_num_splits_lengths", "page_offset",
            "status_string", "lib", "LIB_PATH", "INT8", "BF16", "INT8_HEAD"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -47,6 +47,8 @@ lib.kvq_decode_workspace_bytes.argtypes = [_CP, _i32, _i32, _i32]
 lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
 lib.kvq_choose_num_splits.argtypes = [_CP, _i32, _i32, _i32]
 lib.kvq_choose_num_splits.restype = _i32
+lib.kvq_choose_num_splits_lengths.argtypes = [_CP, _i32, _i32, _P]
+lib.kvq_choose_num_splits_lengths.restype = _i32
 _DEC = [_CP, _P, _P, _i32, _P, _i32, _i32, _i32, _i32, _P, _P, _P, ctypes.c_size_t, _P]
 lib.kvq_decode_attention.argtypes = _DEC
 lib.kvq_decode_attention.restype = ctypes.c_int
@@ -213,6 +215,20 @@ def choose_num_splits(cache: Cache, num_seqs: int, num_q_heads: int, max_context
     r = int(lib.kvq_choose_num_splits(ctypes.byref(cache.desc), num_seqs, num_q_heads, max_context_len))
     if r < 0:
         raise KvqError(r, "kvq_choose_num_splits")
+    return r
+
+
+def choose_num_splits_lengths(cache: Cache, context_lens, num_q_heads: int) -> int:
+    """Split count from the batch's actual lengths (a host sequence of ints, one per sequence)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int64))
+    if lens.ndim != 1 or lens.size == 0 or lens.min() < 0 or lens.max() > 2**31 - 1:
+        raise ValueError("context_lens must be a non-empty 1-D sequence of lengths in [0, 2^31)")
+    lens32 = lens.astype(np.int32)
+    r = int(lib.kvq_choose_num_splits_lengths(ctypes.byref(cache.desc), lens32.size, num_q_heads,
+                                              lens32.ctypes.data_as(ctypes.c_void_p)))
+    if r < 0:
+        raise KvqError(r, "kvq_choose_num_splits_lengths")
     return r
 
 

@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <unordered_set>
 #include <vector>
 
@@ -68,10 +69,14 @@ int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 // minimum number of pages, so that the merge stays small next to the stream.  A single sequence
 // runs best with one workgroup (one wave per SIMD) per compute unit and long page runs per wave.
 // A batch gets two workgroups per compute unit: its sequences' lengths differ, and the second
-// workgroup per CU evens out the longest ones (the host sees only the maximum length).  Both
-// choices come from split-count sweeps of the INT8 and BF16 kernels on 256 CUs (one sequence at
-// 4K and 32K tokens, 4 sequences of 2K-32K, 32 sequences of 512-8K).
-// Several query tokens per sequence (row_tiles > 1): a workgroup holds rtw 16-row tiles of
+// workgroup per CU evens out the longest ones (the host sees only the maximum length).  A batch
+// with fewer (sequence, KV head) pairs than compute units gets four: every split is cpp =
+// max_pages / NS pages long, so a sequence shorter than the maximum fills only its share of its
+// NS splits (the rest exit at once), and with few pairs the longest sequence's splits are the
+// critical path.  These choices come from split-count sweeps of the INT8 and BF16 kernels on 256
+// CUs: one sequence at 4K and 32K tokens; 32 sequences of 512-8K (best at 2); 4 sequences of
+// 2K/8K/16K/32K (best at 128, 5% slower at this rule's 64) and 4 of 32K (best at 64, 14% slower
+// at 128).  Which of the last two a batch is takes its lengths: choose_splits_lengths.// Several query tokens per sequence (row_tiles > 1): a workgroup holds rtw 16-row tiles of
 // (query token, head) pairs, and the count is set by the workgroups per (sequence, KV head), as
 // for one query token.  Workgroups of 4 tiles (one wave per tile) keep no merge scratch in LDS,
 // so two fit on a CU and count as two slots (three for q8_0 prompt sections, whose kernel keeps
@@ -91,6 +96,7 @@ int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus
   const int64_t slots = (int64_t)per_cu * cus;
   const int64_t base = (int64_t)S * Hkv * groups;
   int64_t target_wg = ((int64_t)S * groups > 1 ? 2LL : 1LL) * slots;
+  if (row_tiles == 1 && S > 1 && (int64_t)S * Hkv < cus) target_wg = 4 * slots;  // few pairs
   if (chunks > 1 && target_wg < 4 * slots) target_wg = 4 * slots;
   int64_t ns = (target_wg + base - 1) / base;
   const int min_pages = 8;
@@ -98,6 +104,31 @@ int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus
   if (ns > cap) ns = cap;
   if (ns < 1) ns = 1;
   if (ns > kMaxSplits) ns = kMaxSplits;
+  return (int)ns;
+}
+
+// Split count from the batch's actual lengths (host copy).  One sequence, or at least as many
+// (sequence, KV head) pairs as compute units: as choose_splits.  Fewer pairs: the split length
+// cpp is set so that the non-empty workgroups (sequence s fills ceil(P_s / cpp) splits per KV
+// head) make about four rounds of the compute units, no split shorter than 8 pages, a multiple
+// of 4 pages; NS is then what the longest sequence needs.  Sweeps on 256 CUs: 4 sequences of
+// 2K/8K/16K/32K tokens get 128 splits (the best measured; 137, from 15-page splits, was 3%
+// slower), 4 of 32K get 64 (best).
+int choose_splits_lengths(int dtype, int S, int Hkv, int D, const int32_t *lens, int cus) {
+  int64_t total = 0;
+  int max_len = 0;
+  for (int s = 0; s < S; ++s) {
+    total += (lens[s] + kvq::kPage - 1) / kvq::kPage;
+    max_len = std::max(max_len, (int)lens[s]);
+  }
+  if (max_len <= 0) return 1;
+  if (S == 1 || (int64_t)S * Hkv >= cus) return choose_splits(dtype, S, Hkv, D, max_len, cus);
+  const int min_pages = 8;
+  const int64_t target = 4LL * cus;
+  // (rounded up to a multiple of 4 pages: a split's pages are dealt to the workgroup's 4 waves)
+  const int64_t cpp = (std::max<int64_t>(min_pages, (total * Hkv + target - 1) / target) + 3) / 4 * 4;
+  const int max_pages = (max_len + kvq::kPage - 1) / kvq::kPage;
+  const int64_t ns = std::min<int64_t>(std::max<int64_t>(1, (max_pages + cpp - 1) / cpp), kMaxSplits);
   return (int)ns;
 }
 
@@ -332,6 +363,19 @@ int32_t kvq_choose_num_splits(const kvq_cache_t *cache, int32_t num_seqs, int32_
   if (st != KVQ_OK) return st;
   if (num_seqs <= 0 || max_context_len < 1) return KVQ_ERR_INVALID_ARG;
   return choose_splits(cache->dtype, num_seqs, cache->num_kv_heads, cache->head_dim, max_context_len, device_cus());
+}
+
+int32_t kvq_choose_num_splits_lengths(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
+                                      const int32_t *host_context_lens) {
+  int st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  st = check_heads(cache, num_q_heads);
+  if (st != KVQ_OK) return st;
+  if (num_seqs <= 0 || !host_context_lens) return KVQ_ERR_INVALID_ARG;
+  for (int s = 0; s < num_seqs; ++s)
+    if (host_context_lens[s] < 0) return KVQ_ERR_INVALID_ARG;
+  return choose_splits_lengths(cache->dtype, num_seqs, cache->num_kv_heads, cache->head_dim, host_context_lens,
+                               device_cus());
 }
 
 int kvq_decode_attention(const kvq_cache_t *cache, const void *q, const int32_t *block_tables,

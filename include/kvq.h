@@ -157,6 +157,24 @@ int32_t kvq_choose_num_splits(const kvq_cache_t *cache, int32_t num_seqs, int32_
                               int32_t max_context_len);
 
 /*
+ * Split count from the batch's actual context lengths, for callers that hold them on the host
+ * (the same sources as kvq_choose_num_splits: segments give every compute unit work, and their
+ * best number depends on the lengths).  The decode kernels cut every sequence into segments of
+ * the same length, max_context_len / num_splits, so a sequence shorter than the maximum fills
+ * only part of its segments; kvq_choose_num_splits sees only the maximum and cannot tell a
+ * batch of equal lengths from a ragged one.  Here, for a batch with fewer (sequence, KV head)
+ * pairs than compute units, the segment length is chosen so that the non-empty segments make
+ * about four rounds of the compute units (a multiple of 4 pages, at least 8); otherwise (one
+ * sequence, or many pairs) the result is kvq_choose_num_splits(max length).  Pass it as
+ * num_splits (and to kvq_decode_workspace_bytes).
+ *   host_context_lens  host, int32 [num_seqs], each >= 0 (the lengths the decode will see).
+ * Returns 1..4096, or a negative kvq_status_t on invalid arguments (a null array, a negative
+ * length).  Reads nothing on the device.
+ */
+int32_t kvq_choose_num_splits_lengths(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_q_heads,
+                                      const int32_t *host_context_lens);
+
+/*
  * Split-KV decode attention for one query token per sequence, then the merge.
  *   q                  device, bfloat16 [num_seqs][num_q_heads][D], 16-byte aligned.
  *   block_tables       device, int32 [num_seqs][max_blocks_per_seq].

@@ -178,6 +178,35 @@ def test_split_heuristic_is_sane():
     assert K.lib.kvq_choose_num_splits(ctypes.byref(_desc()), 1, 23, 64) == -1
 
 
+def _by_lengths(desc, lens, Hq):
+    a = np.ascontiguousarray(np.asarray(lens, np.int32))
+    return K.lib.kvq_choose_num_splits_lengths(ctypes.byref(desc), len(a), Hq, a.ctypes.data_as(ctypes.c_void_p))
+
+
+def test_split_count_from_lengths():
+    """With no GPU the library counts 256 compute units (an MI355X's).  A ragged batch of few
+    (sequence, head) pairs gets splits of cpp pages (a multiple of 4) such that the non-empty ones
+    make about four rounds of the CUs: 4 sequences of 2K/8K/16K/32K tokens hold 128 + 512 + 1024 +
+    2048 pages per KV head, x 4 heads / 1024 workgroups -> 14.5 -> cpp 16 -> 2048 / 16 = 128
+    splits; 4 x 32K -> cpp 32 -> 64.  One sequence or many pairs: the same as the maximum-length
+    rule."""
+    d = _desc()
+    assert _by_lengths(d, [2048, 8192, 16384, 32768], 24) == 128
+    assert _by_lengths(d, [32768] * 4, 24) == 64
+    for lens in ([32768], [4096], [512]):
+        assert _by_lengths(d, lens, 24) == K.lib.kvq_choose_num_splits(ctypes.byref(d), 1, 24, max(lens))
+    d8 = _desc(hkv=8, d=128)
+    lens = np.random.default_rng(0).integers(512, 8192, 32)
+    assert _by_lengths(d8, lens, 32) == K.lib.kvq_choose_num_splits(ctypes.byref(d8), 32, 32, int(lens.max()))
+    assert _by_lengths(d, [0, 0], 24) == 1
+    assert _by_lengths(d, [-1, 5], 24) == -1
+    assert _by_lengths(d, [5, 5], 23) == -1
+    assert K.lib.kvq_choose_num_splits_lengths(ctypes.byref(d), 2, 24, None) == -1
+    # every length up to the int32 range stays within 1 .. 4096 splits
+    for lens in ([1, 2**31 - 1], [16] * 3, [2**20, 1, 7]):
+        assert 1 <= _by_lengths(d, lens, 24) <= 4096
+
+
 def test_noalloc_step_rejects_before_launch():
     d = _desc()
     f = K.lib.kvq_decode_step_noalloc

@@ -77,3 +77,12 @@ def test_noalloc_step_checks_its_inputs():
         K.decode_step_noalloc(cache, kv, kv, q, bt.to(torch.int64), cl, 10, 1, out=torch.zeros((1, 2, 128)))
     with pytest.raises(ValueError, match="GPU"):
         K.decode_step_noalloc(cache, kv, kv, q, bt, cl, 10, 1, out=torch.zeros((1, 2, 128)))
+
+
+def test_split_count_from_lengths_checks_its_input():
+    # (refused before the library is called; the values are pinned through the C-ABI)
+    cache, q, bt, cl = _host_problem()
+    with pytest.raises(ValueError, match="lengths"):
+        K.choose_num_splits_lengths(cache, [512, -1], 2)
+    with pytest.raises(ValueError, match="lengths"):
+        K.choose_num_splits_lengths(cache, [], 2)

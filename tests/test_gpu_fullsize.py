@@ -1,7 +1,7 @@
 """GPU parity at the full sizes of the long-context, mixed-batch and dense-8B workloads (one
-layer each), in the launch configuration the benchmark times (the fused step, automatic split
-count): whole-cache byte comparison, and every output row against the oracle, then for each
-swept split count."""
+layer each), in the launch configuration the benchmark times (the fused step at the split count chosen from the
+batch's lengths): whole-cache byte comparison, and every output row against the oracle, then for
+each swept split count and both automatic choices."""
 import numpy as np
 import pytest
 import torch
@@ -28,13 +28,15 @@ def test_fullsize_int8(cid):
     log(f"config {cid}: oracle decode")
     ref = O.decode(pair.o, layer.q, layer.block_tables, layer.context_lens)
     qd, btd, ld = bf16_dev(layer.q), dev(layer.block_tables), dev(layer.context_lens)
-    # the benchmarked step: the new tokens written by the split kernel, automatic split count
+    # the benchmarked step: the new tokens written by the split kernel, the split count from the lengths
     log(f"config {cid}: fused decode step")
-    out, lse = K.decode_step(pair.g, bf16_dev(layer.k[stp]), bf16_dev(layer.v[stp]), qd, btd, ld, mcl, 0)
+    ns_bench = K.choose_num_splits_lengths(pair.g, layer.context_lens, cfg.num_q_heads)
+    out, lse = K.decode_step(pair.g, bf16_dev(layer.k[stp]), bf16_dev(layer.v[stp]), qd, btd, ld, mcl, ns_bench)
     torch.cuda.synchronize()
     pair.assert_cache_equal()
     assert_close(out.cpu().numpy(), lse.cpu().numpy(), ref[0], ref[1], f"config {cid} fused step")
-    for ns in list(cfg.splits) + [0]:
+    # every swept count, the maximum-length choice (0) and the lengths-aware one the benchmark uses
+    for ns in list(cfg.splits) + [0, K.choose_num_splits_lengths(pair.g, layer.context_lens, cfg.num_q_heads)]:
         log(f"config {cid}: decode splits={ns}")
         out, lse = K.decode(pair.g, qd, btd, ld, mcl, ns)
         torch.cuda.synchronize()
