@@ -21,8 +21,10 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 # MFMA results stay in ordinary VGPRs: with AGPRs available (one wave per SIMD) the compiler would
 # otherwise copy the accumulators between the two register files around every VALU update.
+# Leading scalar kernel arguments are preloaded into SGPRs at wave launch (the decode kernels put
+# what their first memory requests need first), which saves the argument-block round trip.
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1", "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def _run(cmd):

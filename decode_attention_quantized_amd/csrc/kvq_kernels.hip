@@ -918,8 +918,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // before anything else; the other buffers fill once Q has arrived.
 template <int D, int NW, int MQR, int FMT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables,
-                            const int32_t *__restrict__ context_lens) {
+void decode_split_i8_kernel(const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
+                            int num_splits, int num_kv_heads, int pages_per_split, int max_blocks,
+                            DecodeArgs args) {
+  // What the first round trip needs (the block table, the lengths and the sizes that place this
+  // workgroup) leads the argument list: the hardware preloads those into scalar registers at
+  // launch, and the rest of the argument block is read during that round trip.
+  DecodeArgs a = args;
+  a.NS = num_splits;
+  a.Hkv = num_kv_heads;
+  a.cpp = pages_per_split;
+  a.max_blocks = max_blocks;
   constexpr bool MQ = MQR > 0;        // several query tokens: rows are (query token, head) pairs
   constexpr int RTW = MQ ? MQR : 1;   // row tiles per workgroup (MQ)
   constexpr int NWP = NW / RTW;       // waves that split the pages of one row tile
@@ -1785,26 +1794,21 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restrict__ o_part,
+                                                           const float2 *__restrict__ mlp,
+                                                           const int32_t *__restrict__ cl, int Hq, int nq, int NS,
+                                                           DecodeArgs a) {
   constexpr int NCH = D / 64;
-  // Every argument is read at the top in one batch: passed through an empty asm (tied operands, no
-  // side effects), they are all loaded before it.  Left alone, the compiler reads each one where it
-  // is first needed and waits there, which serialises round trips before the partials are requested.
-  float *o_part = a.o_part, *outp = a.out, *lsep = a.lse;
-  float2 *mlp = a.ml;
-  const int32_t *cl = a.context_lens;
-  int Hq = a.Hq, nq = a.nq, NS = a.NS, qchunk = a.qchunk, mcl = a.max_context_len, cpp = a.cpp;
-  asm("; merge arguments" : "+s"(o_part), "+s"(outp), "+s"(lsep), "+s"(mlp), "+s"(cl), "+s"(Hq), "+s"(nq), "+s"(NS),
-      "+s"(qchunk), "+s"(mcl), "+s"(cpp));
+  // What the partials' requests need leads the argument list (the hardware preloads it into scalar
+  // registers at launch).  The other arguments are read at the top in one batch: passed through an
+  // empty asm (tied operands, no side effects), they are all loaded before it.  Left alone, the
+  // compiler reads each one where it is first needed and waits there, which adds a round trip.
+  float *outp = a.out, *lsep = a.lse;
+  int qchunk = a.qchunk, mcl = a.max_context_len, cpp = a.cpp;
+  asm("; merge arguments" : "+s"(outp), "+s"(lsep), "+s"(qchunk), "+s"(mcl), "+s"(cpp));
   // (the compiler takes asm results as varying across lanes; they are not)
-  o_part = uniform_ptr(o_part);
   outp = uniform_ptr(outp);
   lsep = uniform_ptr(lsep);
-  mlp = uniform_ptr(mlp);
-  cl = uniform_ptr(cl);
-  Hq = __builtin_amdgcn_readfirstlane(Hq);
-  nq = __builtin_amdgcn_readfirstlane(nq);
-  NS = __builtin_amdgcn_readfirstlane(NS);
   qchunk = __builtin_amdgcn_readfirstlane(qchunk);
   mcl = __builtin_amdgcn_readfirstlane(mcl);
   cpp = __builtin_amdgcn_readfirstlane(cpp);
@@ -1817,8 +1821,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int64_t orow = ((int64_t)s * HQ + hq);
   const int64_t base = orow * NS;
   // buffer loads over this row's partials (past NS they return 0 and are masked below)
-  const auto rml = __builtin_amdgcn_make_buffer_rsrc(mlp + base, 0, NS * 8, 0x00020000);
-  const auto ro = __builtin_amdgcn_make_buffer_rsrc(o_part + base * D, 0, NS * D * 4, 0x00020000);
+  const auto rml = __builtin_amdgcn_make_buffer_rsrc(const_cast<float2 *>(mlp + base), 0, NS * 8, 0x00020000);
+  const auto ro = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(o_part + base * D), 0, NS * D * 4, 0x00020000);
   // the row's query chunk attends over the keys up to its last query token: the context length
   // that sets the row's splits
   const int Lc = cl[s];
@@ -1939,8 +1943,8 @@ static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
   const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, 0, FMT>), dim3(grid), dim3(NW * 64), smem, stream, a,
-                       a.block_tables, a.context_lens);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, 0, FMT>), dim3(grid), dim3(NW * 64), smem, stream, a.block_tables,
+                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
   else
     hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
 }
@@ -1966,14 +1970,14 @@ static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   else if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
     hipLaunchKernelGGL((section_i8_kernel<D, 4, 2>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
   else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a, a.block_tables,
-                       a.context_lens);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a.block_tables,
+                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
   else if (a.rtw == 2)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables,
-                       a.context_lens);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a.block_tables,
+                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
   else
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 1, FMT>), dim3(grid), dim3(256), smem, stream, a, a.block_tables,
-                       a.context_lens);
+    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 1, FMT>), dim3(grid), dim3(256), smem, stream, a.block_tables,
+                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
 }
 
 // dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head
@@ -2002,8 +2006,12 @@ hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t strea
 
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hq * a.nq * (a.D / 64));
-  if (a.D == 256) hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(64), 0, stream, a);
-  else hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(64), 0, stream, a);
+  if (a.D == 256)
+    hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(64), 0, stream, a.o_part, a.ml, a.context_lens, a.Hq,
+                       a.nq, a.NS, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(64), 0, stream, a.o_part, a.ml, a.context_lens, a.Hq,
+                       a.nq, a.NS, a);
   return hipGetLastError();
 }
 
