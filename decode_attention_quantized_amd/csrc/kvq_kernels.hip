@@ -909,6 +909,31 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The decode split kernels take the values that place a workgroup and its first memory requests
+// (block table, context lengths, split and head counts, pages per split, table width, row groups,
+// query chunks) as leading scalar arguments, ahead of the argument block: the hardware preloads
+// them into scalar registers at launch, and the rest of the block is read during the first round
+// trip instead of before it.  placed() makes the kernel's working copy of the block use them.
+#define KVQ_PLACEMENT_PARAMS                                                                              \
+  const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens, int num_splits,     \
+      int num_kv_heads, int pages_per_split, int max_blocks, int row_groups, int chunks, int qchunk, int nq
+__device__ __forceinline__ DecodeArgs placed(const DecodeArgs &args, int num_splits, int num_kv_heads,
+                                             int pages_per_split, int max_blocks, int row_groups, int chunks,
+                                             int qchunk, int nq) {
+  DecodeArgs a = args;
+  a.NS = num_splits;
+  a.Hkv = num_kv_heads;
+  a.cpp = pages_per_split;
+  a.max_blocks = max_blocks;
+  a.row_groups = row_groups;
+  a.chunks = chunks;
+  a.qchunk = qchunk;
+  a.nq = nq;
+  return a;
+}
+#define KVQ_PLACED(args) \
+  placed(args, num_splits, num_kv_heads, pages_per_split, max_blocks, row_groups, chunks, qchunk, nq)
+
 // ---- INT8 cache: 1-page units in a ring of register buffers, f16 MFMA for both products
 //
 // A wave owns pages p0 + wave + k * NW (k = 0, 1, ...) of its split (several query tokens with
@@ -918,17 +943,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // before anything else; the other buffers fill once Q has arrived.
 template <int D, int NW, int MQR, int FMT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_i8_kernel(const int32_t *__restrict__ block_tables, const int32_t *__restrict__ context_lens,
-                            int num_splits, int num_kv_heads, int pages_per_split, int max_blocks,
-                            DecodeArgs args) {
-  // What the first round trip needs (the block table, the lengths and the sizes that place this
-  // workgroup) leads the argument list: the hardware preloads those into scalar registers at
-  // launch, and the rest of the argument block is read during that round trip.
-  DecodeArgs a = args;
-  a.NS = num_splits;
-  a.Hkv = num_kv_heads;
-  a.cpp = pages_per_split;
-  a.max_blocks = max_blocks;
+void decode_split_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
+  const DecodeArgs a = KVQ_PLACED(args);
   constexpr bool MQ = MQR > 0;        // several query tokens: rows are (query token, head) pairs
   constexpr int RTW = MQ ? MQR : 1;   // row tiles per workgroup (MQ)
   constexpr int NWP = NW / RTW;       // waves that split the pages of one row tile
@@ -1361,7 +1377,8 @@ void decode_split_i8_kernel(const int32_t *__restrict__ block_tables, const int3
 // waves per SIMD cover more of each wave's dependency chain).
 template <int D, int NBUF, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
-void section_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
+void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
+  const DecodeArgs a = KVQ_PLACED(args);
   constexpr int NW = 4;                  // waves = row tiles
   constexpr int NG = D / kGroup;         // scale groups
   constexpr int NT = D / 16;             // output tiles
@@ -1386,7 +1403,7 @@ void section_i8_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
   const int s = blockIdx.x / (a.NS * a.row_groups * a.chunks * a.Hkv);
   const int c0 = c * a.qchunk;
   const int n_here = min(a.qchunk, a.nq - c0);
-  const int L_full = max(0, min(a.context_lens[s], a.max_context_len));
+  const int L_full = max(0, min(context_lens[s], a.max_context_len));
   const int L = max(0, L_full - a.nq + c0 + n_here);  // the chunk attends over keys 0 .. L - 1
   const int P = (L + kPage - 1) / kPage;
   const int p0 = j * a.cpp;
@@ -1613,12 +1630,12 @@ __device__ __forceinline__ f4_t mfma16_bf16(s4_t a, s4_t b, f4_t c) {
 
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_bf16_kernel(DecodeArgs a, const int32_t *__restrict__ block_tables) {
+void decode_split_bf16_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
+  const DecodeArgs a = KVQ_PLACED(args);
   constexpr int NG = D / 32;  // 16-byte loads per lane per page (8 bf16 each)
   constexpr int NT = D / 16;
   constexpr int PAGE_B = kPage * D * 2;
   __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];
-  const int32_t *__restrict__ context_lens = a.context_lens;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;
@@ -1938,15 +1955,22 @@ hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// A decode split kernel with its placement arguments ahead of the argument block.
+template <typename Kernel>
+static void launch_placed(Kernel kernel, unsigned grid, unsigned block, size_t smem, hipStream_t stream,
+                          const DecodeArgs &a) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), smem, stream, a.block_tables, a.context_lens, a.NS, a.Hkv,
+                     a.cpp, a.max_blocks, a.row_groups, a.chunks, a.qchunk, a.nq, a);
+}
+
 template <int D, int NW, bool I8, int FMT = 0>
 static void launch_split(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hkv * a.NS);
   const size_t smem = NW > 1 ? (size_t)NW * merge_stride<D>() * sizeof(float) : 0;  // merge scratch
   if constexpr (I8)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, NW, 0, FMT>), dim3(grid), dim3(NW * 64), smem, stream, a.block_tables,
-                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
+    launch_placed(decode_split_i8_kernel<D, NW, 0, FMT>, grid, NW * 64, smem, stream, a);
   else
-    hipLaunchKernelGGL((decode_split_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), smem, stream, a, a.block_tables);
+    launch_placed(decode_split_bf16_kernel<D, NW>, grid, NW * 64, smem, stream, a);
 }
 
 template <int D, bool I8>
@@ -1966,18 +1990,15 @@ static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.chunks * a.Hkv * a.row_groups * a.NS);
   const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);  // LDS merge of a tile's waves
   if (a.rtw == 4 && FMT == 0 && a.chunks > 1)  // q8_0 prompt sections: 3 waves per SIMD
-    hipLaunchKernelGGL((section_i8_kernel<D, 2, 3>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
+    launch_placed(section_i8_kernel<D, 2, 3>, grid, 256, 0, stream, a);
   else if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
-    hipLaunchKernelGGL((section_i8_kernel<D, 4, 2>), dim3(grid), dim3(256), 0, stream, a, a.block_tables);
+    launch_placed(section_i8_kernel<D, 4, 2>, grid, 256, 0, stream, a);
   else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 4, FMT>), dim3(grid), dim3(256), 0, stream, a.block_tables,
-                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
+    launch_placed(decode_split_i8_kernel<D, 4, 4, FMT>, grid, 256, 0, stream, a);
   else if (a.rtw == 2)
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 2, FMT>), dim3(grid), dim3(256), smem, stream, a.block_tables,
-                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
+    launch_placed(decode_split_i8_kernel<D, 4, 2, FMT>, grid, 256, smem, stream, a);
   else
-    hipLaunchKernelGGL((decode_split_i8_kernel<D, 4, 1, FMT>), dim3(grid), dim3(256), smem, stream, a.block_tables,
-                       a.context_lens, a.NS, a.Hkv, a.cpp, a.max_blocks, a);
+    launch_placed(decode_split_i8_kernel<D, 4, 1, FMT>, grid, 256, smem, stream, a);
 }
 
 // dtype: 0 INT8 q8_0, 1 BF16, 2 INT8 per-head
