@@ -144,10 +144,30 @@ __device__ __forceinline__ void q8_codes_div(const float *x, float s, uint32_t *
   }
 }
 
+// The writers take the inputs of their first memory requests (the bf16 rows, the slot mapping and
+// the sizes that place a workgroup) as leading scalar arguments, preloaded into scalar registers at
+// launch; the plane pointers, needed only for the stores, come from the argument block.
+#define KVQ_WRITE_PARAMS                                                                              \
+  const uint16_t *__restrict__ k_rows, const uint16_t *__restrict__ v_rows, const int32_t *__restrict__ slots, \
+      int num_tokens, int num_kv_heads
+__device__ __forceinline__ WriteArgs write_placed(const WriteArgs &args, const uint16_t *k_rows,
+                                                  const uint16_t *v_rows, const int32_t *slots, int num_tokens,
+                                                  int num_kv_heads) {
+  WriteArgs a = args;
+  a.k = k_rows;
+  a.v = v_rows;
+  a.slot_mapping = slots;
+  a.T = num_tokens;
+  a.Hkv = num_kv_heads;
+  return a;
+}
+#define KVQ_WRITE_PLACED(args) write_placed(args, k_rows, v_rows, slots, num_tokens, num_kv_heads)
+
 // Few tokens (fewer than a page: the step of a decode batch): one thread per (token, KV head,
 // K or V, 32-channel group), each storing its group's codes straight into the page.
 template <int D>
-__global__ __launch_bounds__(256) void kv_write_i8_rows_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) void kv_write_i8_rows_kernel(KVQ_WRITE_PARAMS, WriteArgs args) {
+  const WriteArgs a = KVQ_WRITE_PLACED(args);
   constexpr int NG = D / kGroup;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.T * a.Hkv * 2 * NG;
@@ -201,7 +221,8 @@ __global__ __launch_bounds__(256) void kv_write_i8_rows_kernel(WriteArgs a) {
 
 // BF16 cache, few tokens: one thread per (token, KV head, K or V, 8-channel chunk); a scatter copy.
 template <int D>
-__global__ __launch_bounds__(256) void kv_write_bf16_rows_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) void kv_write_bf16_rows_kernel(KVQ_WRITE_PARAMS, WriteArgs args) {
+  const WriteArgs a = KVQ_WRITE_PLACED(args);
   constexpr int NC = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.T * a.Hkv * 2 * NC;
@@ -369,7 +390,8 @@ __device__ __forceinline__ void quant_rows_head(u4_t ka, u4_t kb, u4_t va, u4_t 
 // 32 values); FMT 1: one fp32 scale per (token, KV head).  V pages are staged in LDS: a token's
 // codes spread over the V page at a 4-byte stride, so a whole page is stored at once.
 template <int D, int FMT>
-__global__ __launch_bounds__(D) void kv_write_i8_kernel(WriteArgs a) {
+__global__ __launch_bounds__(D) void kv_write_i8_kernel(KVQ_WRITE_PARAMS, WriteArgs args) {
+  const WriteArgs a = KVQ_WRITE_PLACED(args);
   constexpr int NG = D / kGroup;
   constexpr int NWV = D / 64;
   __shared__ __attribute__((aligned(16))) uint8_t s_v[kPage * D];
@@ -449,7 +471,8 @@ __global__ __launch_bounds__(D) void kv_write_i8_kernel(WriteArgs a) {
 // BF16 cache: a scatter copy with the same windows.  Lane (q, t) of wave i holds the two K-page
 // rows (2i, q, t) and (2i + 1, q, t) (8 channels each); V pages are staged in LDS.
 template <int D>
-__global__ __launch_bounds__(D) void kv_write_bf16_kernel(WriteArgs a) {
+__global__ __launch_bounds__(D) void kv_write_bf16_kernel(KVQ_WRITE_PARAMS, WriteArgs args) {
+  const WriteArgs a = KVQ_WRITE_PLACED(args);
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kPage * D];
   const int b = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, i = threadIdx.x >> 6, q = lane >> 4, t = lane & 15;
@@ -699,7 +722,8 @@ __device__ __forceinline__ void write_new_i8h(const DecodeArgs &a, int64_t page,
 // Per-head INT8 format: one wavefront per (token, KV head, K or V) row; lane l quantizes
 // channels 4l .. 4l + 3 (the scale needs the whole row's maximum).
 template <int D>
-__global__ __launch_bounds__(256) void kv_write_i8h_kernel(WriteArgs a) {
+__global__ __launch_bounds__(256) void kv_write_i8h_kernel(KVQ_WRITE_PARAMS, WriteArgs args) {
+  const WriteArgs a = KVQ_WRITE_PLACED(args);
   const int lane = threadIdx.x & 63;
   const int64_t rid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (rid >= (int64_t)a.T * a.Hkv * 2) return;
@@ -1918,39 +1942,45 @@ hipError_t scratch_address(void **ptr) {
 
 // ------------------------------------------------------------------ launchers
 
+// A writer with its leading arguments ahead of the argument block.
+template <typename Kernel>
+static void launch_write(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, const WriteArgs &a) {
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, a.k, a.v, a.slot_mapping, a.T, a.Hkv, a);
+}
+
 hipError_t launch_kv_write(int dtype, const WriteArgs &a, hipStream_t stream) {
   if (a.T == 0) return hipSuccess;
   if (dtype == 2 && a.T < kPage) {  // per-head INT8, few tokens: one wavefront per row, 4 rows per block
     const unsigned grid = (unsigned)(((int64_t)a.T * a.Hkv * 2 + 3) / 4);
-    if (a.D == 256) hipLaunchKernelGGL(kv_write_i8h_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(kv_write_i8h_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+    if (a.D == 256) launch_write(kv_write_i8h_kernel<256>, dim3(grid), dim3(256), stream, a);
+    else launch_write(kv_write_i8h_kernel<128>, dim3(grid), dim3(256), stream, a);
     return hipGetLastError();
   }
   if (dtype == 2) {
     const dim3 grid((unsigned)((a.T + kPage - 1) / kPage), (unsigned)a.Hkv);
-    if (a.D == 256) hipLaunchKernelGGL((kv_write_i8_kernel<256, 1>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((kv_write_i8_kernel<128, 1>), grid, dim3(128), 0, stream, a);
+    if (a.D == 256) launch_write((kv_write_i8_kernel<256, 1>), grid, dim3(256), stream, a);
+    else launch_write((kv_write_i8_kernel<128, 1>), grid, dim3(128), stream, a);
     return hipGetLastError();
   }
   if (a.T < kPage) {  // no whole page possible: the per-group writers have the shortest latency
     const int per = (dtype == 0 ? a.D / kGroup : a.D / 8) * 2;
     const unsigned grid = (unsigned)(((int64_t)a.T * a.Hkv * per + 255) / 256);
     if (dtype == 0) {
-      if (a.D == 256) hipLaunchKernelGGL(kv_write_i8_rows_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL(kv_write_i8_rows_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+      if (a.D == 256) launch_write(kv_write_i8_rows_kernel<256>, dim3(grid), dim3(256), stream, a);
+      else launch_write(kv_write_i8_rows_kernel<128>, dim3(grid), dim3(256), stream, a);
     } else {
-      if (a.D == 256) hipLaunchKernelGGL(kv_write_bf16_rows_kernel<256>, dim3(grid), dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL(kv_write_bf16_rows_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+      if (a.D == 256) launch_write(kv_write_bf16_rows_kernel<256>, dim3(grid), dim3(256), stream, a);
+      else launch_write(kv_write_bf16_rows_kernel<128>, dim3(grid), dim3(256), stream, a);
     }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((a.T + kPage - 1) / kPage), (unsigned)a.Hkv);
   if (dtype == 0) {
-    if (a.D == 256) hipLaunchKernelGGL((kv_write_i8_kernel<256, 0>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((kv_write_i8_kernel<128, 0>), grid, dim3(128), 0, stream, a);
+    if (a.D == 256) launch_write((kv_write_i8_kernel<256, 0>), grid, dim3(256), stream, a);
+    else launch_write((kv_write_i8_kernel<128, 0>), grid, dim3(128), stream, a);
   } else {
-    if (a.D == 256) hipLaunchKernelGGL(kv_write_bf16_kernel<256>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(kv_write_bf16_kernel<128>, grid, dim3(128), 0, stream, a);
+    if (a.D == 256) launch_write(kv_write_bf16_kernel<256>, grid, dim3(256), stream, a);
+    else launch_write(kv_write_bf16_kernel<128>, grid, dim3(128), stream, a);
   }
   return hipGetLastError();
 }
