@@ -1077,7 +1077,7 @@ void decode_split_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   // contract) writes nothing.  Ordering: vmcnt counts this wave's stores until the memory system
   // has acknowledged them (then a later load of the same bytes, which misses the write-through L1,
   // reads them back), and it retires in issue order; so before requesting page k_last the owner
-  // waits until at most the loads issued after its stores are outstanding (see wait_stores).
+  // waits until at most the loads issued after its stores are outstanding (the waits below).
   bool own_new = !MQ && a.k_new != nullptr && L_raw <= a.max_context_len && p1 == P && wave == (n_units - 1) % NW;
   const int blk_last = own_new ? btrow[P - 1] : 0;  // (only the owner waits for it)
   own_new = own_new && blk_last >= 0 && blk_last < a.NB;
