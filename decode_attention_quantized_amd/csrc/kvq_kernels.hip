@@ -1531,6 +1531,9 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
   // the lane's row (query token c0 + (16 rt + n16) / G) sees keys 0 .. L_row - 1
   const int L_row = L_full - a.nq + c0 + (16 * rt + n16) / a.G + 1;
+  // (wave-uniform) whether this wave's tile holds a real row: with fewer than 49 rows (8 query
+  // tokens at G = 6) the last tile is padding, and its wave only stages pages
+  const bool tile_used = 16 * rt < n_here * a.G;
 
   float m_run = -INFINITY, l_run = 0.0f;
   f4_t acc[NT];
@@ -1632,7 +1635,7 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
     for (int b = 0; b < NBUF; ++b) {
       const int k = k0 + b;
       lds_barrier();
-      process(b & 1, k);
+      if (tile_used) process(b & 1, k);  // (a tile of padding rows only stages)
       stage((b + 1) % NBUF, (b + 1) & 1, k + 1);
       issue((b + 1) % NBUF, k + 1 + NBUF);
     }
