@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--no-multi-token", action="store_true", help="skip the several-query-token decode timings")
     p.add_argument("--no-int-qk", action="store_true", help="skip the integer Q.K timing")
     p.add_argument("--no-other-workloads", action="store_true",
-                   help="skip the fused step of the 4K, mixed-batch and dense-8B workloads")
+                   help="skip the fused step of the tiny 512-token, 4K, mixed-batch and dense-8B workloads")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="CPU seconds for the oracle sample")
     p.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     p.add_argument("--sweep", action="store_true",
@@ -852,7 +852,7 @@ def main():
         del states, host
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        out["other_workloads"] = other_workloads(torch, K, W, [2, 4, 5], max(args.steps // 2, 20), args.warmup,
+        out["other_workloads"] = other_workloads(torch, K, W, [1, 2, 4, 5], max(args.steps // 2, 20), args.warmup,
                                                  not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
