@@ -87,7 +87,7 @@ int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus, int row_tiles = 1,
                   int chunks = 1) {
   (void)D;
-  const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
+  const int64_t max_pages = ((int64_t)max_context_len + kvq::kPage - 1) / kvq::kPage;  // (64-bit: no overflow)
   if (max_pages <= 0) return 1;
   const int rtw = rtw_for(row_tiles), groups = (row_tiles + rtw - 1) / rtw * chunks;
   // workgroups resident at once: 4-tile workgroups fit two per CU, three for q8_0 prompt sections
@@ -118,7 +118,7 @@ int choose_splits_lengths(int dtype, int S, int Hkv, int D, const int32_t *lens,
   int64_t total = 0;
   int max_len = 0;
   for (int s = 0; s < S; ++s) {
-    total += (lens[s] + kvq::kPage - 1) / kvq::kPage;
+    total += ((int64_t)lens[s] + kvq::kPage - 1) / kvq::kPage;  // (64-bit: no overflow near INT32_MAX)
     max_len = std::max(max_len, (int)lens[s]);
   }
   if (max_len <= 0) return 1;
@@ -127,7 +127,7 @@ int choose_splits_lengths(int dtype, int S, int Hkv, int D, const int32_t *lens,
   const int64_t target = 4LL * cus;
   // (rounded up to a multiple of 4 pages: a split's pages are dealt to the workgroup's 4 waves)
   const int64_t cpp = (std::max<int64_t>(min_pages, (total * Hkv + target - 1) / target) + 3) / 4 * 4;
-  const int max_pages = (max_len + kvq::kPage - 1) / kvq::kPage;
+  const int64_t max_pages = ((int64_t)max_len + kvq::kPage - 1) / kvq::kPage;
   const int64_t ns = std::min<int64_t>(std::max<int64_t>(1, (max_pages + cpp - 1) / cpp), kMaxSplits);
   return (int)ns;
 }
@@ -188,7 +188,7 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   if (nq > 1 && ((int64_t)nq * num_q_heads * NS * D * 4 >= INT32_MAX || (int64_t)nq * num_q_heads * D * 2 >= INT32_MAX))
     return KVQ_ERR_INVALID_ARG;
   if (workspace_bytes_given < workspace_bytes(num_seqs * nq, num_q_heads, NS, D)) return KVQ_ERR_WORKSPACE_TOO_SMALL;
-  const int max_pages = (max_context_len + kvq::kPage - 1) / kvq::kPage;
+  const int64_t max_pages = ((int64_t)max_context_len + kvq::kPage - 1) / kvq::kPage;
   a.q = static_cast<const uint16_t *>(q);
   a.kc = cache->k;
   a.vc = cache->v;
@@ -212,7 +212,7 @@ int prepare_decode(const kvq_cache_t *cache, const void *q, const int32_t *block
   a.G = num_q_heads / Hkv;
   a.NB = cache->num_blocks;
   a.NS = NS;
-  a.cpp = (max_pages + NS - 1) / NS;
+  a.cpp = (int)((max_pages + NS - 1) / NS);
   a.D = D;
   a.waves = waves_for(cache->dtype, D);
   a.nq = nq;
@@ -308,7 +308,7 @@ int check_decode_impl(const kvq_cache_t *cache, const void *k_new, const void *v
   for (int i = 0; i < num_seqs; ++i) {
     const int32_t L = lens[i];
     if (L < 0 || L > max_context_len) return KVQ_ERR_VALIDATION_FAILED;
-    const int pages = (L + kvq::kPage - 1) / kvq::kPage;
+    const int pages = (int)(((int64_t)L + kvq::kPage - 1) / kvq::kPage);
     for (int p = 0; p < pages; ++p) {
       const int32_t b = tables[(size_t)i * max_blocks_per_seq + p];
       if (b < 0 || b >= cache->num_blocks) return KVQ_ERR_VALIDATION_FAILED;
@@ -318,7 +318,7 @@ int check_decode_impl(const kvq_cache_t *cache, const void *k_new, const void *v
   }
   if (k_new) {  // no other sequence may read a block that receives a new token
     for (int i = 0; i < num_seqs; ++i) {
-      const int pages = (lens[i] + kvq::kPage - 1) / kvq::kPage;
+      const int pages = (int)(((int64_t)lens[i] + kvq::kPage - 1) / kvq::kPage);
       for (int p = 0; p + 1 < pages; ++p)
         if (new_blocks.count(tables[(size_t)i * max_blocks_per_seq + p])) return KVQ_ERR_VALIDATION_FAILED;
     }
