@@ -1395,10 +1395,10 @@ void decode_split_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
 // LDS and runs the decode kernel's page step on its own tile (Q.K per group and fp16 scale,
 // online softmax, P' = p * s_v as f16 hi + lo, P.V).  LDS holds two pages, so the stores of page
 // k + 1 never meet the reads of page k - 1; each thread holds a quarter or an eighth of a page in
-// registers, so NBUF pages are in flight at little register cost.  Two forms: 4 pages in flight
-// at 2 waves per SIMD (one chunk of query tokens, e.g. a decode of 6 to 10 tokens), and 2 pages in
-// flight with the registers capped for 3 waves per SIMD (prompt sections: many chunks, where more
-// waves per SIMD cover more of each wave's dependency chain).
+// registers, so NBUF pages are in flight at little register cost.  Two forms, both with 2 pages in
+// flight: registers uncapped (one chunk of query tokens, e.g. a decode of 6 to 10 tokens, whose
+// grid puts two workgroups on a CU), and registers capped for 3 waves per SIMD (prompt sections:
+// many chunks, where more waves per SIMD cover more of each wave's dependency chain).
 template <int D, int NBUF, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
 void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
@@ -2025,7 +2025,7 @@ static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   if (a.rtw == 4 && FMT == 0 && a.chunks > 1)  // q8_0 prompt sections: 3 waves per SIMD
     launch_placed(section_i8_kernel<D, 2, 3>, grid, 256, 0, stream, a);
   else if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
-    launch_placed(section_i8_kernel<D, 4, 2>, grid, 256, 0, stream, a);
+    launch_placed(section_i8_kernel<D, 2, 2>, grid, 256, 0, stream, a);
   else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
     launch_placed(decode_split_i8_kernel<D, 4, 4, FMT>, grid, 256, 0, stream, a);
   else if (a.rtw == 2)
