@@ -1795,13 +1795,13 @@ void decode_split_bf16_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
 //
 // One wavefront per (64-channel chunk, output row, sequence); an output row is a (query token,
 // query head) pair (one query token per sequence unless nq > 1).  The splits are taken 64 at a
-// time: lane j loads split j's (m, l) and every lane loads its channel of all 64 partial outputs,
-// all in one round trip.  The block's maximum and weights w_j = 2^(m_j - M) come from wave
-// reductions, each lane folds the 64 partials with the weights broadcast from their lanes, and
-// blocks beyond the first (more than 64 splits) are folded with the online softmax's rescaling.
-// Only the splits that hold pages count (their number follows from the row's context length,
-// read alongside the partials):  out = o / l;  lse = ln 2 * (M + log2 l).
-constexpr int kMergeBlock = 64;
+// time (MB = 8, 16, 32 or 64: the smallest that holds all splits, so few splits cost few loads):
+// lane j loads split j's (m, l) and every lane loads its channel of all MB partial outputs, all in
+// one round trip.  The block's maximum and weights w_j = 2^(m_j - M) come from wave reductions,
+// each lane folds the MB partials with the weights broadcast from their lanes, and blocks beyond
+// the first (more than 64 splits) are folded with the online softmax's rescaling.  Only the
+// splits that hold pages count (their number follows from the row's context length, read
+// alongside the partials):  out = o / l;  lse = ln 2 * (M + log2 l).
 
 // Reductions over a wavefront: DPP within each 16-lane row (pairs, quads, half rows, rows), then
 // the four row results read into scalars.
@@ -1837,7 +1837,7 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
   return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
 }
 
-template <int D>
+template <int D, int MB>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restrict__ o_part,
                                                            const float2 *__restrict__ mlp,
                                                            const int32_t *__restrict__ cl, int Hq, int nq, int NS,
@@ -1873,11 +1873,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restric
   const int qi = hq / Hq;  // query token of the row
   const int c0 = qi - qi % qchunk, n_here = min(qchunk, nq - c0);
   float M = -INFINITY, l = 0.0f, o = 0.0f;
-  for (int j0 = 0; j0 < NS; j0 += kMergeBlock) {
+  static_assert(MB >= 8 && MB <= 64 && (MB & (MB - 1)) == 0, "split block: 8, 16, 32 or 64");
+  for (int j0 = 0; j0 < NS; j0 += MB) {
     const u2_t w = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, lane * 8, j0 * 8, 0));
-    float ov[kMergeBlock];
+    float ov[MB];
 #pragma unroll
-    for (int u = 0; u < kMergeBlock; ++u)
+    for (int u = 0; u < MB; ++u)
       ov[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, c * 4, (j0 + u) * D * 4, 0));
     // (read here, after the partial loads are issued: the wait for the context length then does
     // not hold them back)
@@ -1886,7 +1887,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restric
     const int nsa = min(NS, ((L + kPage - 1) / kPage + cpp - 1) / cpp);  // splits with pages
     // splits past nsa were not written by this call: their (m, l, o) are masked, never multiplied
     const int nb = nsa - j0;
-    const bool valid = lane < nb;
+    const bool valid = lane < nb && lane < MB;  // (lanes past the block read the next one's)
     const float mj = valid ? __uint_as_float(w[0]) : -INFINITY;
     const float Mn = fmaxf(M, wave_max(mj));
     const float Mr = (Mn == -INFINITY) ? 0.0f : Mn;  // (no key yet: any finite reference)
@@ -1894,12 +1895,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float *__restric
     const float wj = exp2_w(mj - Mr);                  // mj = -inf: 0
     l = fmaf(l, alpha, wave_sum(valid ? wj * __uint_as_float(w[1]) : 0.0f));
     float acc = o * alpha;
-    if (nb >= kMergeBlock) {
+    if (nb >= MB) {
 #pragma unroll
-      for (int u = 0; u < kMergeBlock; ++u) acc = fmaf(row_lane(wj, u), ov[u], acc);
+      for (int u = 0; u < MB; ++u) acc = fmaf(row_lane(wj, u), ov[u], acc);
     } else {
 #pragma unroll
-      for (int u = 0; u < kMergeBlock; ++u) acc = fmaf(row_lane(wj, u), (u < nb) ? ov[u] : 0.0f, acc);
+      for (int u = 0; u < MB; ++u) acc = fmaf(row_lane(wj, u), (u < nb) ? ov[u] : 0.0f, acc);
     }
     o = acc;
     M = Mn;
@@ -2058,14 +2059,24 @@ hipError_t launch_decode_split(int dtype, const DecodeArgs &a, hipStream_t strea
   return hipGetLastError();
 }
 
+template <int D, int MB>
+static void launch_merge(const DecodeArgs &a, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_merge_kernel<D, MB>), dim3(grid), dim3(64), 0, stream, a.o_part, a.ml, a.context_lens,
+                     a.Hq, a.nq, a.NS, a);
+}
+
+template <int D>
+static void launch_merge_mb(const DecodeArgs &a, unsigned grid, hipStream_t stream) {
+  if (a.NS <= 8) launch_merge<D, 8>(a, grid, stream);
+  else if (a.NS <= 16) launch_merge<D, 16>(a, grid, stream);
+  else if (a.NS <= 32) launch_merge<D, 32>(a, grid, stream);
+  else launch_merge<D, 64>(a, grid, stream);
+}
+
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.Hq * a.nq * (a.D / 64));
-  if (a.D == 256)
-    hipLaunchKernelGGL(decode_merge_kernel<256>, dim3(grid), dim3(64), 0, stream, a.o_part, a.ml, a.context_lens, a.Hq,
-                       a.nq, a.NS, a);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(64), 0, stream, a.o_part, a.ml, a.context_lens, a.Hq,
-                       a.nq, a.NS, a);
+  if (a.D == 256) launch_merge_mb<256>(a, grid, stream);
+  else launch_merge_mb<128>(a, grid, stream);
   return hipGetLastError();
 }
 
