@@ -253,7 +253,9 @@ def test_decode_ragged_batch_interleaved_pages():
     pair = Pair("int8", layer.num_blocks, cfg.num_kv_heads, cfg.head_dim)
     fill_from_layer(pair, layer)
     pair.assert_cache_equal()
-    _check_decode(pair, layer.q, layer.block_tables, layer.context_lens, [1, 4, 8, 33, 0], "ragged interleaved")
+    # (split counts that fill the merge's blocks of 8, 16, 32 and 64 splits in part)
+    _check_decode(pair, layer.q, layer.block_tables, layer.context_lens, [1, 4, 8, 12, 20, 33, 0],
+                  "ragged interleaved")
 
 
 def test_write_then_decode_stream_order():
