@@ -30,6 +30,7 @@ namespace kvq {
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
@@ -68,6 +69,11 @@ __device__ __forceinline__ h8_t i8x8_to_h8(uint32_t w0, uint32_t w1) {
 
 __device__ __forceinline__ f4_t mfma_f16(h8_t a, h8_t b, f4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// The K = 16 form: a lane's four K slots are its own four rows of B (four tokens of a page).
+__device__ __forceinline__ f4_t mfma16_f16(h4_t a, h4_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f4_t mfma_bf16(b8_t a, b8_t b, f4_t c) {
@@ -1393,7 +1399,8 @@ void decode_split_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
 // thread), converts them to the f16 MFMA fragments and stores them in LDS, and waves 0 and 1 stage
 // the K and V scale tiles.  After one barrier every wave reads the fragments of all groups from
 // LDS and runs the decode kernel's page step on its own tile (Q.K per group and fp16 scale,
-// online softmax, P' = p * s_v as f16 hi + lo, P.V).  LDS holds two pages, so the stores of page
+// online softmax, P' = p * s_v as f16 hi + lo, P.V as two K = 16 products, hi then lo, on one
+// read of each V operand, which LDS holds once).  LDS holds two pages, so the stores of page
 // k + 1 never meet the reads of page k - 1; each thread holds a quarter or an eighth of a page in
 // registers, so NBUF pages are in flight at little register cost.  Two forms, both with 2 pages in
 // flight: registers uncapped (one chunk of query tokens, e.g. a decode of 6 to 10 tokens, whose
@@ -1413,7 +1420,7 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   constexpr int SDW = SCALE_B / 4;
   static_assert(CPT >= 1 && (NBUF & 1) == 0, "page split and LDS double buffer");
   __shared__ __attribute__((aligned(16))) h8_t s_k[2][NG][64];     // K fragments [group][lane]
-  __shared__ __attribute__((aligned(16))) u4_t s_v[2][NT][64];     // V operands [tile][lane] (codes twice)
+  __shared__ __attribute__((aligned(16))) u2_t s_v[2][NT][64];     // V operands [tile][lane] (4 codes)
   __shared__ __attribute__((aligned(16))) uint32_t s_sc[2][2][SDW];  // K, V scale tiles, token-quad-major
   __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];   // rescale factors, per row
 
@@ -1476,7 +1483,7 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
         for (int e = 0; e < 4; ++e) {
           uint32_t v0, v1;
           i8x4_to_f16(w[e], v0, v1);
-          s_v[lb][4 * i + e][lane] = u4_t{v0, v1, v0, v1};  // the P.V operand as it is read
+          s_v[lb][4 * i + e][lane] = u2_t{v0, v1};  // the P.V operand as it is read
         }
       }
     }
@@ -1611,12 +1618,16 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
       const h2_t hi01 = ph01 * s01, hi23 = ph23 * s23;
       const h2_t lo01 = __builtin_elementwise_fma(pl01, s01, __builtin_elementwise_fma(ph01, s01, -hi01));
       const h2_t lo23 = __builtin_elementwise_fma(pl23, s23, __builtin_elementwise_fma(ph23, s23, -hi23));
-      const h8_t pp = __builtin_bit_cast(h8_t, u4_t{__builtin_bit_cast(uint32_t, hi01), __builtin_bit_cast(uint32_t, hi23),
-                                                   __builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
+      // two K = 16 products on one read of the V operand (hi, then lo): the 8-byte operand is
+      // read from LDS once, where the K = 32 form packing hi and lo needs the codes twice
+      const h4_t ph = __builtin_bit_cast(h4_t, u2_t{__builtin_bit_cast(uint32_t, hi01), __builtin_bit_cast(uint32_t, hi23)});
+      const h4_t pl = __builtin_bit_cast(h4_t, u2_t{__builtin_bit_cast(uint32_t, lo01), __builtin_bit_cast(uint32_t, lo23)});
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int jt = 2 * g + jj;
-        acc[jt] = mfma_f16(pp, __builtin_bit_cast(h8_t, s_v[lb][jt][lane]), acc[jt]);
+        const h4_t vb = __builtin_bit_cast(h4_t, s_v[lb][jt][lane]);
+        acc[jt] = mfma16_f16(ph, vb, acc[jt]);
+        acc[jt] = mfma16_f16(pl, vb, acc[jt]);
       }
     }
   };
