@@ -76,7 +76,8 @@ int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 // critical path.  These choices come from split-count sweeps of the INT8 and BF16 kernels on 256
 // CUs: one sequence at 4K and 32K tokens; 32 sequences of 512-8K (best at 2); 4 sequences of
 // 2K/8K/16K/32K (best at 128, 5% slower at this rule's 64) and 4 of 32K (best at 64, 14% slower
-// at 128).  Which of the last two a batch is takes its lengths: choose_splits_lengths.// Several query tokens per sequence (row_tiles > 1): a workgroup holds rtw 16-row tiles of
+// at 128).  Which of the last two a batch is takes its lengths: choose_splits_lengths.
+// Several query tokens per sequence (row_tiles > 1): a workgroup holds rtw 16-row tiles of
 // (query token, head) pairs, and the count is set by the workgroups per (sequence, KV head), as
 // for one query token.  Workgroups of 4 tiles (one wave per tile) keep no merge scratch in LDS,
 // so two fit on a CU and count as two slots (three for q8_0 prompt sections, whose kernel keeps
