@@ -5,7 +5,10 @@ counts and query-token counts are drawn from one seeded generator. Each case run
 point through the C ABI, on a cache filled through kvq_write:
 - decode: kvq_decode_attention, for the q8_0, BF16 and per-head caches;
 - step: kvq_decode_step, whose split kernel writes each sequence's last token;
-- mq: kvq_decode_attention_mq, several query tokens, for the q8_0 and per-head caches.
+- mq: kvq_decode_attention_mq, several query tokens, for the q8_0 and per-head caches;
+- int8qk: kvq_decode_attention_int8qk (q8_0), against the oracle's quantized-query definition;
+- noalloc: kvq_decode_step_noalloc, the fused step with the library's own partials buffer (shapes
+  drawn so that the partials fit it).
 
 Each case is compared with the oracle's plain definition over the oracle's own cache, which was
 written from the same rows: |gpu - oracle| <= 2e-3 + 1e-3 |oracle| for every output and lse
@@ -57,7 +60,26 @@ def _draw_cases():
     return cases
 
 
-CASES = _draw_cases()
+def _draw_extra_cases():
+    rng = np.random.default_rng(20261203)
+    cases = []
+    for i in range(NUM_EXTRA):
+        op = ("int8qk", "noalloc")[i % 2]
+        D = int(rng.choice([128, 256]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.integers(1, 9))
+        S = int(rng.integers(1, 4))
+        lens = [int(rng.choice([0, 1, 15, 16, 17])) if rng.integers(0, 4) == 0 else int(rng.integers(3, 1800))
+                for _ in range(S)]
+        dtype = "int8" if op == "int8qk" else str(rng.choice(["int8", "bf16", "int8_head"]))
+        splits = int(rng.choice([0, 1, 3, 7, 16]))
+        cases.append(dict(i=NUM_CASES + i, seed=int(rng.integers(1 << 30)), op=op, D=D, Hkv=Hkv, Hq=G * Hkv,
+                          lens=lens, dtype=dtype, splits=splits, nq=1))
+    return cases
+
+
+NUM_EXTRA = 30
+CASES = _draw_cases() + _draw_extra_cases()
 
 
 def _build(seed, lens, Hq, Hkv, D, dtype, nq):
@@ -112,11 +134,21 @@ def test_random_case(case):
         out, lse = K.decode_step(pair.g, bf16_dev(last[0]), bf16_dev(last[1]), bf16_dev(q), dev(bt), dev(lens), mcl,
                                  c["splits"])
         ref = O.decode(pair.o, q, bt, lens)
+    elif c["op"] == "noalloc":
+        O.kv_write(pair.o, last[0], last[1], slots)
+        out = torch.empty((len(lens), c["Hq"], c["D"]), dtype=torch.float32, device="cuda")
+        lse = torch.empty((len(lens), c["Hq"]), dtype=torch.float32, device="cuda")
+        K.decode_step_noalloc(pair.g, bf16_dev(last[0]), bf16_dev(last[1]), bf16_dev(q), dev(bt), dev(lens), mcl,
+                              c["splits"], out=out, lse=lse)
+        ref = O.decode(pair.o, q, bt, lens)
     else:
         pair.write(last[0], last[1], slots)
         if c["op"] == "mq":
             out, lse = K.decode_mq(pair.g, bf16_dev(q), dev(bt), dev(lens), mcl, c["splits"])
             ref = O.decode_mq(pair.o, q, bt, lens)
+        elif c["op"] == "int8qk":
+            out, lse = K.decode(pair.g, bf16_dev(q), dev(bt), dev(lens), mcl, c["splits"], int_qk=True)
+            ref = O.decode_int8_qk(pair.o, q, bt, lens)
         else:
             out, lse = K.decode(pair.g, bf16_dev(q), dev(bt), dev(lens), mcl, c["splits"])
             ref = O.decode(pair.o, q, bt, lens)
