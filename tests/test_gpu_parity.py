@@ -253,8 +253,9 @@ def test_decode_ragged_batch_interleaved_pages():
     pair = Pair("int8", layer.num_blocks, cfg.num_kv_heads, cfg.head_dim)
     fill_from_layer(pair, layer)
     pair.assert_cache_equal()
-    # (split counts that fill the merge's blocks of 8, 16, 32 and 64 splits in part)
-    _check_decode(pair, layer.q, layer.block_tables, layer.context_lens, [1, 4, 8, 12, 20, 33, 0],
+    # (split counts that fill the merge's blocks of 8, 16, 32 and 64 splits in part, and the
+    # largest count the library takes: 4096, nearly all of them empty)
+    _check_decode(pair, layer.q, layer.block_tables, layer.context_lens, [1, 4, 8, 12, 20, 33, 4096, 0],
                   "ragged interleaved")
 
 
