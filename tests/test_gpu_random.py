@@ -9,6 +9,7 @@ point through the C ABI, on a cache filled through kvq_write:
 - int8qk: kvq_decode_attention_int8qk (q8_0), against the oracle's quantized-query definition;
 - noalloc: kvq_decode_step_noalloc, the fused step with the library's own partials buffer (shapes
   drawn so that the partials fit it).
+A last group draws wide batches (32 to 128 sequences of up to 300 tokens).
 
 Each case is compared with the oracle's plain definition over the oracle's own cache, which was
 written from the same rows: |gpu - oracle| <= 2e-3 + 1e-3 |oracle| for every output and lse
@@ -78,8 +79,28 @@ def _draw_extra_cases():
     return cases
 
 
+def _draw_batch_cases():
+    """Wide batches: 32 to 128 sequences of 0 to 300 tokens."""
+    rng = np.random.default_rng(20261204)
+    cases = []
+    for i in range(NUM_BATCH):
+        op = ("decode", "step", "mq")[i % 3]
+        D = int(rng.choice([128, 256]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.integers(1, 9))
+        S = int(rng.integers(32, 129))
+        lens = [int(x) for x in rng.integers(0, 301, S)]
+        dtype = str(rng.choice(["int8", "int8_head"] if op == "mq" else ["int8", "bf16", "int8_head"]))
+        splits = int(rng.choice([0, 1, 2, 5]))
+        nq = int(rng.choice([2, 4, 9])) if op == "mq" else 1
+        cases.append(dict(i=NUM_CASES + NUM_EXTRA + i, seed=int(rng.integers(1 << 30)), op=op, D=D, Hkv=Hkv,
+                          Hq=G * Hkv, lens=lens, dtype=dtype, splits=splits, nq=nq))
+    return cases
+
+
 NUM_EXTRA = 30
-CASES = _draw_cases() + _draw_extra_cases()
+NUM_BATCH = 9
+CASES = _draw_cases() + _draw_extra_cases() + _draw_batch_cases()
 
 
 def _build(seed, lens, Hq, Hkv, D, dtype, nq):
