@@ -1805,7 +1805,7 @@ void decode_split_bf16_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
 // ------------------------------------------------------------------ decode: merge
 //
 // One wavefront per (64-channel chunk, output row, sequence); an output row is a (query token,
-// query head) pair (one query token per sequence unless nq > 1).  The splits are taken 64 at a
+// query head) pair (one query token per sequence unless nq > 1).  The splits are taken MB at a
 // time (MB = 8, 16, 32 or 64: the smallest that holds all splits, so few splits cost few loads):
 // lane j loads split j's (m, l) and every lane loads its channel of all MB partial outputs, all in
 // one round trip.  The block's maximum and weights w_j = 2^(m_j - M) come from wave reductions,
