@@ -75,7 +75,7 @@ int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 // NS splits (the rest exit at once), and with few pairs the longest sequence's splits are the
 // critical path.  These choices come from split-count sweeps of the INT8 and BF16 kernels on 256
 // CUs: one sequence at 4K and 32K tokens; 32 sequences of 512-8K (best at 2); 4 sequences of
-// 2K/8K/16K/32K (best at 128, 5% slower at this rule's 64) and 4 of 32K (best at 64, 14% slower
+// 2K/8K/16K/32K (best at 128, 6% slower at this rule's 64) and 4 of 32K (best at 64, 14% slower
 // at 128).  Which of the last two a batch is takes its lengths: choose_splits_lengths.
 // Several query tokens per sequence (row_tiles > 1): a workgroup holds rtw 16-row tiles of
 // (query token, head) pairs, and the count is set by the workgroups per (sequence, KV head), as
