@@ -81,10 +81,12 @@ int rtw_for(int row_tiles) { return row_tiles >= 3 ? 4 : row_tiles; }
 // (query token, head) pairs, and the count is set by the workgroups per (sequence, KV head), as
 // for one query token.  Workgroups of 4 tiles (one wave per tile) keep no merge scratch in LDS,
 // so two fit on a CU and count as two slots (three for q8_0 prompt sections, whose kernel keeps
-// its registers within 3 waves per SIMD).  Prompt sections (several query chunks) get at
-// least four rounds of workgroups, so that the last, partly filled round is short.  Sweeps at
-// 32K: 8 query tokens run best at 128 splits (two workgroups per CU); a 2048-token section takes
-// 6.3 ms at 1 split, 5.5 ms at 2 and 5.1 ms at 4 (this rule gives 3).
+// its registers within 3 waves per SIMD).  A q8_0 single chunk of 3 or 4 tiles runs as one
+// 8-wave workgroup per CU (two page groups), one slot.  Prompt sections (several query chunks)
+// get at least four rounds of workgroups, so that the last, partly filled round is short.
+// Sweeps at 32K: 8 query tokens run best at 64 splits of the two-group form (48 and 96 are 19%
+// and 45% slower); a 2048-token section takes 6.3 ms at 1 split, 5.5 ms at 2 and 5.1 ms at 4
+// (this rule gives 3).
 int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus, int row_tiles = 1,
                   int chunks = 1) {
   (void)D;
@@ -92,8 +94,9 @@ int choose_splits(int dtype, int S, int Hkv, int D, int max_context_len, int cus
   if (max_pages <= 0) return 1;
   const int rtw = rtw_for(row_tiles), groups = (row_tiles + rtw - 1) / rtw * chunks;
   // workgroups resident at once: 4-tile workgroups fit two per CU, three for q8_0 prompt sections
-  // (their kernel is capped at 3 waves' registers per SIMD)
-  const int per_cu = (row_tiles > 1 && rtw == 4) ? (dtype == KVQ_INT8_Q8_0 && chunks > 1 ? 3 : 2) : 1;
+  // (their kernel is capped at 3 waves' registers per SIMD); a q8_0 single chunk's 8-wave
+  // workgroup fills a CU
+  const int per_cu = (row_tiles > 1 && rtw == 4) ? (dtype == KVQ_INT8_Q8_0 ? (chunks > 1 ? 3 : 1) : 2) : 1;
   const int64_t slots = (int64_t)per_cu * cus;
   const int64_t base = (int64_t)S * Hkv * groups;
   int64_t target_wg = ((int64_t)S * groups > 1 ? 2LL : 1LL) * slots;

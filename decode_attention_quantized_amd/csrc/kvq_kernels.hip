@@ -1403,11 +1403,16 @@ void decode_split_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
 // read of each V operand, which LDS holds once).  LDS holds two pages, so the stores of page
 // k + 1 never meet the reads of page k - 1; each thread holds a quarter or an eighth of a page in
 // registers, so NBUF pages are in flight at little register cost.  Two forms, both with 2 pages in
-// flight: registers uncapped (one chunk of query tokens, e.g. a decode of 6 to 10 tokens, whose
-// grid puts two workgroups on a CU), and registers capped for 3 waves per SIMD (prompt sections:
-// many chunks, where more waves per SIMD cover more of each wave's dependency chain).
-template <int D, int NBUF, int WPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE)))
+// flight:
+// - PG = 2 page groups of 4 waves, registers uncapped (one chunk of query tokens, e.g. a decode
+//   of 6 to 10 tokens): group g takes pages 2 i + g of the split, each group with its own LDS
+//   buffers, and at the end group 1's tiles are folded into group 0's through LDS.  The 8 waves
+//   fill a CU as two 4-wave workgroups of half the split length would, with half as many
+//   partials for the merge to read;
+// - PG = 1, registers capped for 3 waves per SIMD (prompt sections: many chunks, where more
+//   waves per SIMD cover more of each wave's dependency chain).
+template <int D, int NBUF, int WPE, int PG>
+__global__ __launch_bounds__(256 * PG) __attribute__((amdgpu_waves_per_eu(WPE)))
 void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   const DecodeArgs a = KVQ_PLACED(args);
   constexpr int NW = 4;                  // waves = row tiles
@@ -1419,13 +1424,16 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   constexpr int SCALE_B = kPage * NG * 2;  // bytes of one scale tile
   constexpr int SDW = SCALE_B / 4;
   static_assert(CPT >= 1 && (NBUF & 1) == 0, "page split and LDS double buffer");
-  __shared__ __attribute__((aligned(16))) h8_t s_k[2][NG][64];     // K fragments [group][lane]
-  __shared__ __attribute__((aligned(16))) u2_t s_v[2][NT][64];     // V operands [tile][lane] (4 codes)
-  __shared__ __attribute__((aligned(16))) uint32_t s_sc[2][2][SDW];  // K, V scale tiles, token-quad-major
-  __shared__ __attribute__((aligned(16))) float s_alpha[NW][16];   // rescale factors, per row
+  static_assert(PG == 1 || PG == 2, "page groups");
+  __shared__ __attribute__((aligned(16))) h8_t s_k[PG][2][NG][64];     // K fragments [group][lane]
+  __shared__ __attribute__((aligned(16))) u2_t s_v[PG][2][NT][64];     // V operands [tile][lane] (4 codes)
+  __shared__ __attribute__((aligned(16))) uint32_t s_sc[PG][2][2][SDW];  // K, V scale tiles, token-quad-major
+  __shared__ __attribute__((aligned(16))) float s_alpha[NW * PG][16];  // rescale factors, per row
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW - 1);  // (0 .. 3: lets the compiler fix each chunk's plane)
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) & (NW * PG - 1);
+  const int wave = wave_all & (NW - 1);  // (0 .. 3: lets the compiler fix each chunk's plane)
+  const int pg = PG > 1 ? wave_all / NW : 0;  // page group: pages PG i + pg
   const int rt = wave;  // this wave's row tile
   const int n16 = lane & 15, q4 = lane >> 4;
   const int j = blockIdx.x % a.NS;
@@ -1452,7 +1460,8 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   // load cc / 64 of that lane), and one dword of a scale tile (wave 0: K, wave 1: V)
   u4_t cb[NBUF][CPT];
   uint32_t sb[NBUF];
-  auto issue = [&](int b, int k) {
+  auto issue = [&](int b, int i) {
+    const int k = PG * i + pg;
     const bool ok = k < n_units;  // (past the split: size-0 resources, the loads return zeros)
     const int64_t page = page_of(k);
 #pragma unroll
@@ -1468,7 +1477,8 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   };
   // restaged scale dword of tile dword l (group-major [group][token] -> [token quad][group][token])
   const int st_dw = (((lane & 7) >> 1) * NG + (lane >> 3)) * 2 + (lane & 1);
-  auto stage = [&](int b, int lb, int k) {
+  auto stage = [&](int b, int lb, int i) {
+    const int k = PG * i + pg;
 #pragma unroll
     for (int ci = 0; ci < CPT; ++ci) {
       const int id0 = wave * 64 + NW * 64 * ci;
@@ -1476,14 +1486,14 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
       const int i = (is_v ? id0 - CH : id0) >> 6;  // the decode kernel's load index
       const u4_t w = cb[b][ci];
       if (!is_v) {
-        s_k[lb][2 * i][lane] = i8x8_to_h8(w[0], w[1]);
-        s_k[lb][2 * i + 1][lane] = i8x8_to_h8(w[2], w[3]);
+        s_k[pg][lb][2 * i][lane] = i8x8_to_h8(w[0], w[1]);
+        s_k[pg][lb][2 * i + 1][lane] = i8x8_to_h8(w[2], w[3]);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           uint32_t v0, v1;
           i8x4_to_f16(w[e], v0, v1);
-          s_v[lb][4 * i + e][lane] = u2_t{v0, v1};  // the P.V operand as it is read
+          s_v[pg][lb][4 * i + e][lane] = u2_t{v0, v1};  // the P.V operand as it is read
         }
       }
     }
@@ -1496,7 +1506,7 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
       const int t0 = 2 * (lane & 7);
       sw &= (t0 < lim ? 0xFFFFu : 0u) | (t0 + 1 < lim ? 0xFFFF0000u : 0u);
     }
-    if (wave < 2 && lane < SDW) s_sc[lb][wave][st_dw] = sw;
+    if (wave < 2 && lane < SDW) s_sc[pg][lb][wave][st_dw] = sw;
   };
   auto lds_barrier = [] {  // LDS-only fences: the page loads in flight are not waited for
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -1547,7 +1557,7 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
 #pragma unroll
   for (int jt = 0; jt < NT; ++jt) acc[jt] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
   auto scales = [&](int lb, int which, u2_t (&out)[NG]) {
-    const u4_t *src = reinterpret_cast<const u4_t *>(&s_sc[lb][which][q4 * NG * 2]);
+    const u4_t *src = reinterpret_cast<const u4_t *>(&s_sc[pg][lb][which][q4 * NG * 2]);
 #pragma unroll
     for (int i = 0; i < NG / 2; ++i) {
       const u4_t w = src[i];
@@ -1557,7 +1567,8 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   };
 
   // One page from LDS buffer lb: Q.K^T, one online-softmax update, P.V (the decode kernel's step).
-  auto process = [&](int lb, int k) {
+  auto process = [&](int lb, int i) {
+    const int k = PG * i + pg;
     // valid tokens of the page for this lane's row
     const int lim_row = k < n_units ? min(max(L_row - (p0 + k) * kPage, 0), kPage) : 0;
     u2_t ksc[NG];
@@ -1571,10 +1582,10 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
       sc[3] = fma_h16hi(sw[1], cg[3], sc[3]);
       pin4(sc);
     };
-    f4_t c_prev = mfma_f16(s_k[lb][0][lane], qop[0], f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+    f4_t c_prev = mfma_f16(s_k[pg][lb][0][lane], qop[0], f4_t{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
     for (int g = 1; g < NG; ++g) {
-      const f4_t cg = mfma_f16(s_k[lb][g][lane], qop[g], f4_t{0.0f, 0.0f, 0.0f, 0.0f});
+      const f4_t cg = mfma_f16(s_k[pg][lb][g][lane], qop[g], f4_t{0.0f, 0.0f, 0.0f, 0.0f});
       scale_group(g - 1, c_prev);
       c_prev = cg;
     }
@@ -1598,8 +1609,8 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
     l_run = l_run * alpha + psum;
     m_run = m_new;
     if (__any(grew)) {  // some row's maximum grew: rescale its accumulator rows
-      if (q4 == 0) s_alpha[wave][n16] = alpha;
-      const f4_t ar = *reinterpret_cast<const f4_t *>(&s_alpha[wave][4 * q4]);
+      if (q4 == 0) s_alpha[wave_all][n16] = alpha;
+      const f4_t ar = *reinterpret_cast<const f4_t *>(&s_alpha[wave_all][4 * q4]);
 #pragma unroll
       for (int jt = 0; jt < NT; ++jt) acc[jt] *= ar;
     }
@@ -1625,7 +1636,7 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int jt = 2 * g + jj;
-        const h4_t vb = __builtin_bit_cast(h4_t, s_v[lb][jt][lane]);
+        const h4_t vb = __builtin_bit_cast(h4_t, s_v[pg][lb][jt][lane]);
         acc[jt] = mfma16_f16(ph, vb, acc[jt]);
         acc[jt] = mfma16_f16(pl, vb, acc[jt]);
       }
@@ -1641,15 +1652,57 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   // the buffers in fixed registers and the waits for each page exact.
   stage(0, 0, 0);
   issue(0, NBUF);
-  for (int k0 = 0; k0 < n_units; k0 += NBUF) {
+  const int n_steps = (n_units + PG - 1) / PG;  // pages per group (the same trip count for every wave)
+  for (int i0 = 0; i0 < n_steps; i0 += NBUF) {
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) {
-      const int k = k0 + b;
+      const int i = i0 + b;
       lds_barrier();
-      if (tile_used) process(b & 1, k);  // (a tile of padding rows only stages)
-      stage((b + 1) % NBUF, (b + 1) & 1, k + 1);
-      issue((b + 1) % NBUF, k + 1 + NBUF);
+      if (tile_used) process(b & 1, i);  // (a tile of padding rows only stages)
+      stage((b + 1) % NBUF, (b + 1) & 1, i + 1);
+      issue((b + 1) % NBUF, i + 1 + NBUF);
     }
+  }
+  if constexpr (PG > 1) {
+    // Two page groups: group 1's tiles (accumulators over the staging buffers, and (m, l) per row)
+    // are folded into group 0's, each weighted by 2^(m - M) per row with M the larger maximum; group
+    // 0 then stores the tile's partial as one group would.
+    __shared__ float s_xm[2][NW][16], s_xl[NW][16];
+    lds_barrier();  // every wave is done with the staging buffers
+    const float l_row = rows_sum(l_run);
+    if (q4 == 0) {
+      s_xm[pg][rt][n16] = m_run;
+      if (pg == 1) s_xl[rt][n16] = l_row;
+    }
+    f4_t *xk = reinterpret_cast<f4_t *>(&s_k[0][0][0][0]);  // tiles 0 .. NT / 2 - 1
+    f4_t *xv = reinterpret_cast<f4_t *>(&s_v[0][0][0][0]);  // tiles NT / 2 .. NT - 1
+    if (pg == 1 && tile_used) {
+#pragma unroll
+      for (int jt = 0; jt < NT / 2; ++jt) xk[(rt * (NT / 2) + jt) * 64 + lane] = acc[jt];
+#pragma unroll
+      for (int jt = NT / 2; jt < NT; ++jt) xv[(rt * (NT / 2) + jt - NT / 2) * 64 + lane] = acc[jt];
+    }
+    lds_barrier();
+    if (pg == 1 || !tile_used) return;
+    const f4_t m0r = *reinterpret_cast<const f4_t *>(&s_xm[0][rt][4 * q4]);
+    const f4_t m1r = *reinterpret_cast<const f4_t *>(&s_xm[1][rt][4 * q4]);
+    f4_t w0, w1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float M = fmaxf(m0r[r], m1r[r]);
+      w0[r] = (m0r[r] == -INFINITY) ? 0.0f : exp2_w(m0r[r] - M);  // (a group without keys: 0)
+      w1[r] = (m1r[r] == -INFINITY) ? 0.0f : exp2_w(m1r[r] - M);
+    }
+#pragma unroll
+    for (int jt = 0; jt < NT / 2; ++jt) acc[jt] = acc[jt] * w0 + xk[(rt * (NT / 2) + jt) * 64 + lane] * w1;
+#pragma unroll
+    for (int jt = NT / 2; jt < NT; ++jt) acc[jt] = acc[jt] * w0 + xv[(rt * (NT / 2) + jt - NT / 2) * 64 + lane] * w1;
+    const float m1 = s_xm[1][rt][n16], l1 = s_xl[rt][n16];
+    const float Mn = fmaxf(m_run, m1);
+    const float a0 = (m_run == -INFINITY) ? 0.0f : exp2_w(m_run - Mn);
+    const float a1 = (m1 == -INFINITY) ? 0.0f : exp2_w(m1 - Mn);
+    m_run = Mn;
+    l_run = (q4 == 0) ? fmaf(a0, l_row, a1 * l1) : 0.0f;  // (summed over the row's lanes when stored)
   }
   // The epilogue takes its lane indices from a fresh lane count (behind an opaque mask, so that it
   // is not merged with the prologue's): keeping the prologue's lane-derived values live across the
@@ -2035,9 +2088,9 @@ static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.chunks * a.Hkv * a.row_groups * a.NS);
   const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);  // LDS merge of a tile's waves
   if (a.rtw == 4 && FMT == 0 && a.chunks > 1)  // q8_0 prompt sections: 3 waves per SIMD
-    launch_placed(section_i8_kernel<D, 2, 3>, grid, 256, 0, stream, a);
-  else if (a.rtw == 4 && FMT == 0)  // q8_0: the workgroup loads and converts each page once
-    launch_placed(section_i8_kernel<D, 2, 2>, grid, 256, 0, stream, a);
+    launch_placed(section_i8_kernel<D, 2, 3, 1>, grid, 256, 0, stream, a);
+  else if (a.rtw == 4 && FMT == 0)  // q8_0 single chunk: two page groups of 4 waves
+    launch_placed(section_i8_kernel<D, 2, 2, 2>, grid, 512, 0, stream, a);
   else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
     launch_placed(decode_split_i8_kernel<D, 4, 4, FMT>, grid, 256, 0, stream, a);
   else if (a.rtw == 2)
