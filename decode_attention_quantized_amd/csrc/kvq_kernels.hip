@@ -2081,20 +2081,20 @@ static void launch_split_nw(const DecodeArgs &a, hipStream_t stream) {
   }
 }
 
-// Several query tokens per sequence (INT8 cache, 4 waves): one workgroup per (16-row tile, split,
-// KV head, sequence).
+// Several query tokens per sequence (INT8 cache): one workgroup per (group of rtw 16-row tiles,
+// split, KV head, query chunk, sequence).
 template <int D, int FMT>
 static void launch_split_mq(const DecodeArgs &a, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)a.S * a.chunks * a.Hkv * a.row_groups * a.NS);
-  const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);  // LDS merge of a tile's waves
+  const size_t smem = (size_t)4 * merge_stride<D>() * sizeof(float);  // LDS merge of 4 waves' tiles
   if (a.rtw == 4 && FMT == 0 && a.chunks > 1)  // q8_0 prompt sections: 3 waves per SIMD
     launch_placed(section_i8_kernel<D, 2, 3, 1>, grid, 256, 0, stream, a);
   else if (a.rtw == 4 && FMT == 0)  // q8_0 single chunk: two page groups of 4 waves
     launch_placed(section_i8_kernel<D, 2, 2, 2>, grid, 512, 0, stream, a);
   else if (a.rtw == 4)  // (one wave per tile: no merge scratch, so several workgroups share a CU)
     launch_placed(decode_split_i8_kernel<D, 4, 4, FMT>, grid, 256, 0, stream, a);
-  else if (a.rtw == 2)
-    launch_placed(decode_split_i8_kernel<D, 4, 2, FMT>, grid, 256, smem, stream, a);
+  else if (a.rtw == 2)  // (8 waves, 4 per tile: twice the waves per SIMD at the same split count)
+    launch_placed(decode_split_i8_kernel<D, 8, 2, FMT>, grid, 512, 2 * smem, stream, a);
   else
     launch_placed(decode_split_i8_kernel<D, 4, 1, FMT>, grid, 256, smem, stream, a);
 }
