@@ -111,3 +111,16 @@ def test_prompt_sections(nq):
 def test_prompt_section_dense_geometry():
     pair, q, bt, lens = _problem(2400, [300, 1000], 32, 8, 128, 64)
     _check(pair, q, bt, lens, [2, 0], "prompt section G=4 D=128 nq=64")
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,nq", [(256, 24, 4, 4), (256, 24, 4, 8), (256, 24, 4, 10), (128, 32, 8, 5),
+                                         (128, 32, 8, 9), (128, 16, 1, 3)])
+def test_mq_short_splits(D, Hq, Hkv, nq):
+    """Splits of one to three pages.  In the two-tile workgroup (4 waves per tile) and the
+    single-chunk one (two page groups) some waves or a whole group then hold only pages past the
+    split, and the first query tokens' rows have no keys in the later splits: the folds inside
+    the workgroup must give those parts weight 0."""
+    lens = [nq, nq + 15, 40, 48, 100, 129]
+    pair, q, bt, lens = _problem(2500 + D + Hq + nq, lens, Hq, Hkv, D, nq)
+    mp = (int(lens.max()) + PAGE - 1) // PAGE  # pages of the longest sequence
+    _check(pair, q, bt, lens, [mp, (mp + 1) // 2, (mp + 2) // 3, 0], f"short splits D={D} Hq={Hq} Hkv={Hkv} nq={nq}")
