@@ -551,12 +551,17 @@ typedef short s4_t __attribute__((ext_vector_type(4)));
 // Register buffers (pages in flight + the page being processed) of the INT8 split kernel.
 constexpr int kI8Buffers = 2;
 
-// Max / sum over the four lane rows (lanes n, n+16, n+32, n+48) with the gfx950 row swaps.
+// Max / sum over the four lane rows (lanes n, n+16, n+32, n+48) with the gfx950 row swaps.  The
+// max is a comparison, not fmaxf: the swapped values are not known to be canonical floats, so
+// fmaxf would first quiet each of them (two more instructions per step).  A NaN score still
+// reaches the output through its weight.
 __device__ __forceinline__ float rows_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float a0 = __uint_as_float(a[0]), a1 = __uint_as_float(a[1]);
+  x = a0 > a1 ? a0 : a1;
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const float b0 = __uint_as_float(b[0]), b1 = __uint_as_float(b[1]);
+  return b0 > b1 ? b0 : b1;
 }
 
 __device__ __forceinline__ float rows_sum(float x) {
@@ -1091,6 +1096,7 @@ void decode_split_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   // MQ: the lane's row sees keys 0 .. L - nq + token (causal among the query tokens)
   int L_row = L;
   if constexpr (MQ) L_row = L_full - a.nq + c0 + (16 * rt + n16) / a.G + 1;
+  const int L_min = L_full - a.nq + c0 + 1;  // (MQ) the chunk's first query token's limit, the smallest
   __builtin_amdgcn_sched_barrier(0);
   const int64_t page_new = (int64_t)blk_last * a.Hkv + h;
   const int t_new = (L - 1) & (kPage - 1);
@@ -1271,8 +1277,13 @@ void decode_split_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
     float x[4];
     int lim_row = lim;  // valid tokens of the page for this lane's row
     if constexpr (MQ) lim_row = u < n_units ? min(max(L_row - (p0 + u) * kPage, 0), kPage) : 0;
+    if (MQ && u < n_units && (p0 + u + 1) * kPage <= L_min) {  // (uniform) every row sees the whole page
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim_row) ? sc[i] * cmul : -INFINITY;
+      for (int i = 0; i < 4; ++i) x[i] = sc[i] * cmul;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim_row) ? sc[i] * cmul : -INFINITY;
+    }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -1548,6 +1559,7 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
   const float cmul = ldexpf(kLog2e / sqrtf((float)D), -shift);
   // the lane's row (query token c0 + (16 rt + n16) / G) sees keys 0 .. L_row - 1
   const int L_row = L_full - a.nq + c0 + (16 * rt + n16) / a.G + 1;
+  const int L_min = L_full - a.nq + c0 + 1;  // the chunk's first query token's limit (the smallest)
   // (wave-uniform) whether this wave's tile holds a real row: with fewer than 49 rows (8 query
   // tokens at G = 6) the last tile is padding, and its wave only stages pages
   const bool tile_used = 16 * rt < n_here * a.G;
@@ -1591,8 +1603,13 @@ void section_i8_kernel(KVQ_PLACEMENT_PARAMS, DecodeArgs args) {
     }
     scale_group(NG - 1, c_prev);
     float x[4];
+    if (k < n_units && (p0 + k + 1) * kPage <= L_min) {  // (uniform) every row sees the whole page
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim_row) ? sc[i] * cmul : -INFINITY;
+      for (int i = 0; i < 4; ++i) x[i] = sc[i] * cmul;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (4 * q4 + i < lim_row) ? sc[i] * cmul : -INFINITY;
+    }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
