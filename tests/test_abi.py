@@ -207,6 +207,19 @@ def test_split_count_from_lengths():
         assert 1 <= _by_lengths(d, lens, 24) <= 4096
 
 
+def test_split_count_several_tokens():
+    """With no GPU the library counts 256 compute units.  One 32K sequence, 24/4 heads: 2 and 4
+    query tokens (one and two row tiles) and a q8_0 chunk of 3 or 4 tiles (8 tokens) fill the
+    CUs once, one workgroup each, at 64 splits; the per-head format's 4-tile workgroups fit two
+    per CU (128); a 2048-token section (205 chunks of 10 tokens, three workgroups per CU) gets at
+    least four rounds: 3072 workgroups over 820 (chunk, KV head) groups -> 4 splits."""
+    d = _desc()
+    for nq, ns in [(2, 64), (4, 64), (8, 64), (10, 64), (2048, 4)]:
+        assert K.lib.kvq_choose_num_splits_mq(ctypes.byref(d), 1, nq, 24, 32768) == ns, nq
+    dh = _desc(dtype=K.INT8_HEAD)
+    assert K.lib.kvq_choose_num_splits_mq(ctypes.byref(dh), 1, 8, 24, 32768) == 128
+
+
 def test_noalloc_step_rejects_before_launch():
     d = _desc()
     f = K.lib.kvq_decode_step_noalloc
