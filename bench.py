@@ -289,6 +289,7 @@ def time_split_kernel(torch, K, layers, mcl, ns, ws, passes):
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_i8_long32k_hbm_traffic.md")
 FILL_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kv_write_i8_long32k_fill_hbm_traffic.md")
+SECTION_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "section_i8_2048_long32k_hbm_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_kernels.hip")
 
 
@@ -316,10 +317,14 @@ def measured_traffic(path=None):
 COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes
 
 
+SECTION_TOKENS = 2048  # the prompt section bench.py times (the last 2048 tokens of the 32K context)
+
+
 def pmc_workload(args):
     """Runs what the HBM-traffic counters are taken on: the prefill fill of every layer's cache
-    (one kvq_write each, at set-up), a plain copy kernel of known size (the calibration), then
-    the decode_split launches of every layer, a few times each."""
+    (one kvq_write each, at set-up), a plain copy kernel of known size (the calibration), the
+    decode_split launches of every layer, a few times each, then one 2048-token prompt section
+    over the first layer."""
     import torch
 
     import decode_attention_quantized_amd as K
@@ -343,10 +348,17 @@ def pmc_workload(args):
         for L in layers:
             K.decode_partials(L.cache, L.q, L.bt, L.lens, mcl, ns, ws)
     torch.cuda.synchronize()
-    log(f"pmc workload done: splits {ns}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    qs = torch.randn((S, SECTION_TOKENS, Hq, cfg.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    L0 = layers[0]
+    K.decode_mq(L0.cache, qs, L0.bt, L0.lens, mcl, 0)
+    torch.cuda.synchronize()
+    log(f"pmc workload done: splits {ns}, and a {SECTION_TOKENS}-token section")
 
 
-def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, algorithmic, title, path):
+def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, algorithmic, title, path,
+                     workload="long-32k layer: batch 1, context 32768, 24/4 heads, head_dim 256", note=""):
     """Per-dispatch medians of FETCH_SIZE and WRITE_SIZE for the kernels whose name holds `tag`,
     scaled by what the same counters read for the calibration copy; written to `path`."""
     import csv
@@ -373,7 +385,7 @@ def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, al
     kf, kw = COPY_BYTES / fc, COPY_BYTES / wc
     rec = {
         "kernel": kernel,
-        "workload": "long-32k layer: batch 1, context 32768, 24/4 heads, head_dim 256",
+        "workload": workload,
         "kernel_source_sha256": kernel_source_digest(),
         "fetch_kib_per_launch_raw": round(fs / 1024, 1), "write_kib_per_launch_raw": round(ws_ / 1024, 1),
         "copy_fetch_kib_raw": round(fc / 1024, 1), "copy_write_kib_raw": round(wc / 1024, 1),
@@ -400,6 +412,7 @@ def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, al
         f"| copy FETCH_SIZE | {fc / 1024:.1f} | | {COPY_BYTES} |",
         f"| copy WRITE_SIZE | {wc / 1024:.1f} | | {COPY_BYTES} |",
         "",
+        *([note, ""] if note else []),
         f"Algorithmic bytes per launch: {algorithmic}; measured / algorithmic = "
         f"{(fs * kf + ws_ * kw) / algorithmic:.3f}.  The record below is what bench.py reads (it reports",
         "it only while the kernel source still has the digest it was taken on):",
@@ -429,6 +442,24 @@ def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
                      "kv_write_i8_kernel<256, 0>", fill_bytes(T, cfg.num_kv_heads, cfg.head_dim, "int8"),
                      f"# HBM traffic: kv_write_i8_kernel<256, 0> (q8_0), prefill fill of a long-32k layer ({T} tokens, "
                      "4 KV heads, D 256)", FILL_TRAFFIC_SUMMARY)
+    # The prompt section: every chunk of 10 query tokens reads the cache up to its own last token,
+    # so the kernel requests the prefix once per chunk (205 times).  Its algorithmic bytes count
+    # each input once (cache, Q) and the partials written once: what HBM must carry if the repeated
+    # reads are served from the caches.
+    Hq, D, Hkv = cfg.num_q_heads, cfg.head_dim, cfg.num_kv_heads
+    ns = 4
+    sec_alg = int(algorithmic_bytes(lens, Hkv, D, "int8") + SECTION_TOKENS * Hq * D * 2
+                  + SECTION_TOKENS * Hq * ns * (D * 4 + 8))
+    _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, "section_i8_kernel<256, 2, 3, 1>",
+                     "section_i8_kernel", sec_alg,
+                     f"# HBM traffic: section_i8_kernel<256, 2, 3, 1> (q8_0), a {SECTION_TOKENS}-token prompt section "
+                     "over a long-32k layer", SECTION_TRAFFIC_SUMMARY,
+                     workload=f"long-32k layer: the last {SECTION_TOKENS} of 32768 tokens as query tokens, "
+                              f"24/4 heads, head_dim 256, {ns} splits",
+                     note=(f"Algorithmic bytes count the cache ({int(algorithmic_bytes(lens, Hkv, D, 'int8'))} B), "
+                           f"the query block ({SECTION_TOKENS * Hq * D * 2} B) and the partials "
+                           f"({SECTION_TOKENS * Hq * ns * (D * 4 + 8)} B) once each; the kernel requests the "
+                           "cache once per 10-token chunk, 205 times."))
 
 
 def oracle_cache_for(O, lay, k, v):
