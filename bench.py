@@ -290,6 +290,7 @@ def time_split_kernel(torch, K, layers, mcl, ns, ws, passes):
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_split_i8_long32k_hbm_traffic.md")
 FILL_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kv_write_i8_long32k_fill_hbm_traffic.md")
 SECTION_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "section_i8_2048_long32k_hbm_traffic.md")
+EIGHT_TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "section_i8_8tok_long32k_hbm_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_quantized_amd", "csrc", "kvq_kernels.hip")
 
 
@@ -323,8 +324,8 @@ SECTION_TOKENS = 2048  # the prompt section bench.py times (the last 2048 tokens
 def pmc_workload(args):
     """Runs what the HBM-traffic counters are taken on: the prefill fill of every layer's cache
     (one kvq_write each, at set-up), a plain copy kernel of known size (the calibration), the
-    decode_split launches of every layer, a few times each, then one 2048-token prompt section
-    over the first layer."""
+    decode_split launches of every layer, a few times each, then decodes of 4 and 8 query tokens
+    (three each) and one 2048-token prompt section over the first layer."""
     import torch
 
     import decode_attention_quantized_amd as K
@@ -350,17 +351,22 @@ def pmc_workload(args):
     torch.cuda.synchronize()
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
-    qs = torch.randn((S, SECTION_TOKENS, Hq, cfg.head_dim), generator=g, device="cuda").to(torch.bfloat16)
     L0 = layers[0]
+    for nq in (4, 8):
+        qm = torch.randn((S, nq, Hq, cfg.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+        for _ in range(3):
+            K.decode_mq(L0.cache, qm, L0.bt, L0.lens, mcl, 0)
+    qs = torch.randn((S, SECTION_TOKENS, Hq, cfg.head_dim), generator=g, device="cuda").to(torch.bfloat16)
     K.decode_mq(L0.cache, qs, L0.bt, L0.lens, mcl, 0)
     torch.cuda.synchronize()
-    log(f"pmc workload done: splits {ns}, and a {SECTION_TOKENS}-token section")
+    log(f"pmc workload done: splits {ns}, decodes of 4 and 8 query tokens, and a {SECTION_TOKENS}-token section")
 
 
 def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, algorithmic, title, path,
                      workload="long-32k layer: batch 1, context 32768, 24/4 heads, head_dim 256", note=""):
-    """Per-dispatch medians of FETCH_SIZE and WRITE_SIZE for the kernels whose name holds `tag`,
-    scaled by what the same counters read for the calibration copy; written to `path`."""
+    """Per-dispatch medians of FETCH_SIZE and WRITE_SIZE for the kernel whose name (with its
+    template arguments) starts `tag`, scaled by what the same counters read for the calibration
+    copy; written to `path`."""
     import csv
 
     def per_dispatch(path_, counter):
@@ -370,7 +376,10 @@ def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, al
                 if r["Counter_Name"] != counter:
                     continue
                 v = float(r["Counter_Value"]) * 1024.0  # KiB -> bytes
-                if tag in r["Kernel_Name"]:
+                name = r["Kernel_Name"]
+                if name.startswith("void kvq::"):
+                    name = name[len("void kvq::"):]
+                if name.startswith(tag):
                     mine.append(v)
                 elif "bitwise_not" in r["Kernel_Name"]:
                     copy.append(v)
@@ -414,8 +423,8 @@ def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, al
         "",
         *([note, ""] if note else []),
         f"Algorithmic bytes per launch: {algorithmic}; measured / algorithmic = "
-        f"{(fs * kf + ws_ * kw) / algorithmic:.3f}.  The record below is what bench.py reads (it reports",
-        "it only while the kernel source still has the digest it was taken on):",
+        f"{(fs * kf + ws_ * kw) / algorithmic:.3f}.  The record below holds the digest of the kernel source",
+        "it was taken on (bench.py reports a record only while the source still has that digest):",
         "",
         json.dumps(rec),
         "",
@@ -427,14 +436,14 @@ def _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, kernel, tag, al
 
 
 def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
-    """Turns the two counter runs of pmc_workload into the traffic summaries bench.py reads: the
-    decode_split launches, and the prefill fill's kvq_write launches (one 32767-token write per
-    layer at set-up)."""
+    """Turns the two counter runs of pmc_workload into the traffic summaries: the decode_split
+    launches and the prefill fill's kvq_write launches (one 32767-token write per layer at set-up),
+    which bench.py reads, and the 2048-token prompt section and the 8-token decode."""
     import workloads as W
     cfg = W.CONFIGS[3]
     lens = np.array(cfg.context_lens)
     _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, "decode_split_i8_kernel<256, 4, 0, 0>",
-                     "decode_split_i8_kernel", algorithmic_bytes(lens, cfg.num_kv_heads, cfg.head_dim, "int8"),
+                     "decode_split_i8_kernel<256, 4, 0, 0>", algorithmic_bytes(lens, cfg.num_kv_heads, cfg.head_dim, "int8"),
                      "# HBM traffic: decode_split_i8_kernel<256, 4, 0, 0> (q8_0), long-32k layer (context 32768, "
                      "24/4 heads, D 256)", TRAFFIC_SUMMARY)
     T = int(lens[0]) - 1
@@ -451,7 +460,7 @@ def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
     sec_alg = int(algorithmic_bytes(lens, Hkv, D, "int8") + SECTION_TOKENS * Hq * D * 2
                   + SECTION_TOKENS * Hq * ns * (D * 4 + 8))
     _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, "section_i8_kernel<256, 2, 3, 1>",
-                     "section_i8_kernel", sec_alg,
+                     "section_i8_kernel<256, 2, 3, 1>", sec_alg,
                      f"# HBM traffic: section_i8_kernel<256, 2, 3, 1> (q8_0), a {SECTION_TOKENS}-token prompt section "
                      "over a long-32k layer", SECTION_TRAFFIC_SUMMARY,
                      workload=f"long-32k layer: the last {SECTION_TOKENS} of 32768 tokens as query tokens, "
@@ -460,6 +469,19 @@ def pmc_summarize(fetch_csv, write_csv, cmd_fetch, cmd_write):
                            f"the query block ({SECTION_TOKENS * Hq * D * 2} B) and the partials "
                            f"({SECTION_TOKENS * Hq * ns * (D * 4 + 8)} B) once each; the kernel requests the "
                            "cache once per 10-token chunk, 205 times."))
+    # The decode of 8 query tokens per sequence (one chunk, 64 splits of the two-page-group form):
+    # the cache and Q read once, the partials written once.
+    nq8, ns8 = 8, 64
+    dec8_alg = int(algorithmic_bytes(lens, Hkv, D, "int8") + nq8 * Hq * D * 2 + nq8 * Hq * ns8 * (D * 4 + 8))
+    _traffic_summary(fetch_csv, write_csv, cmd_fetch, cmd_write, "section_i8_kernel<256, 2, 2, 2>",
+                     "section_i8_kernel<256, 2, 2, 2>", dec8_alg,
+                     "# HBM traffic: section_i8_kernel<256, 2, 2, 2> (q8_0), a decode of 8 query tokens over a "
+                     "long-32k layer", EIGHT_TRAFFIC_SUMMARY,
+                     workload=f"long-32k layer: the last {nq8} of 32768 tokens as query tokens, 24/4 heads, "
+                              f"head_dim 256, {ns8} splits",
+                     note=(f"Algorithmic bytes count the cache ({int(algorithmic_bytes(lens, Hkv, D, 'int8'))} B), "
+                           f"the query block ({nq8 * Hq * D * 2} B) and the partials "
+                           f"({nq8 * Hq * ns8 * (D * 4 + 8)} B) once each."))
 
 
 def oracle_cache_for(O, lay, k, v):
