@@ -68,12 +68,14 @@ def _mq_queries(n, Hq, D, seed):
     return W.f32_to_bf16_bits((rng.standard_normal((1, n, Hq, D)) * mult).astype(np.float32))
 
 
-@pytest.mark.parametrize("nq,sample,context", [(8, None, None), (2048, 24, None), (65536, 24, 66560)])
+@pytest.mark.parametrize("nq,sample,context", [(2, None, None), (4, None, None), (8, None, None), (2048, 24, None),
+                                                (65536, 24, 66560)])
 def test_fullsize_several_query_tokens(nq, sample, context):
     """The long-context layer with n_q query tokens at the end of the sequence, in the launch
-    configuration the benchmark times (automatic split count): 8 tokens (a verification step) and a
-    2048-token prompt section; and the largest n_q the library takes, 65536, over a 66560-token
-    sequence.  Every row of the 8-token decode, and every head of a seeded sample of the longer
+    configuration the benchmark times (automatic split count): 2, 4 and 8 tokens (verification
+    steps; one 16-row tile, two tiles, and the two-page-group form of four tiles) and a 2048-token
+    prompt section; and the largest n_q the library takes, 65536, over a 66560-token sequence.
+    Every row of the 2-, 4- and 8-token decodes, and every head of a seeded sample of the longer
     runs' query tokens (first and last included), against the oracle: query token i of n attends to
     the first L - n + i + 1 keys."""
     layer = W.make_layer(3, 0) if context is None else W.make_layer(3, 0, context_lens=(context,))
