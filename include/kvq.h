@@ -241,7 +241,18 @@ int kvq_decode_attention_int8qk(const kvq_cache_t *cache, const void *q, const i
                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_splits, float *out, float *lse,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* Split count kvq_decode_attention_mq uses for num_splits == 0 (negative status on error). */
+/*
+ * Split count kvq_decode_attention_mq uses for num_splits == 0 (negative status on error).
+ * Half-the-memory page, section "Read the compressed cache without copying it first": the pages
+ * tune the split count (segments) for verification separately from one-token decode; long-context
+ * page, section "Split count": it depends on the context length.  The rule is the one-token rule
+ * (enough workgroups to cover the compute units, at least 8 pages per split) counted in the
+ * workgroups this path launches, each holding up to 4 row tiles of (query token, head) pairs.  The
+ * compute units' workgroup slots are counted as: one per CU for a q8_0 single chunk of 3 or 4 row
+ * tiles (6 to 10 tokens at 6 query heads per KV head: one 8-wave workgroup fills a CU), three for
+ * q8_0 prompt sections (which also get at least four rounds of workgroups), two for the other
+ * workgroups of 3 or 4 tiles, and one otherwise.  Arguments as kvq_decode_attention_mq.
+ */
 int32_t kvq_choose_num_splits_mq(const kvq_cache_t *cache, int32_t num_seqs, int32_t num_query_tokens,
                                  int32_t num_q_heads, int32_t max_context_len);
 
